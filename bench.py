@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of paged decode attention on one MI355X.
+
+One step = one decode step of a whole model's attention layers: for each of
+`--layers` layers (each with its own K/V pool, so no layer's data can still be
+in L2 / MALL when it is read) append one new token per sequence
+(pa_reshape_and_cache) and run pa_decode over every sequence's paged context.
+
+Default workload: Llama-2-7B-shaped decode -- 64 sequences, 32 q heads = 32 kv
+heads x 128, fp16, block size 16, context lengths uniform in [1, 2048], pool =
+needed blocks + 10 %, 32 layers.  Inputs are synthetic (seeded normal draws).
+
+Prints ONE JSON line.  `value` is KV GB/s (bytes of K and V the decode calls
+must read, over the whole timed region); the line also carries seq*layers/s,
+the roofline of the decode call, and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention KV GB/s (% of HBM peak) and seq-layers/s, 1×MI355X"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b",
+                    choices=["llama7b", "llama70b_gqa", "mixed_bs8", "mixed_bs16", "mixed_bs32", "shared_prefix"])
+    ap.add_argument("--layers", type=int, default=None, help="default: 32 (7B-shaped), 80 (70B-shaped)")
+    ap.add_argument("--partition-tokens", type=int, default=None,
+                    help="0 = library's choice, -1 = single pass, N = split-K partition (default: the workload's)")
+    ap.add_argument("--layout", choices=["bhtd", "bthd"], default="bhtd")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, target_s):
+    """Time the CPU oracle (as it is) on a bounded sample of the same workload."""
+    import oracle
+    threads = oracle.num_threads()
+    S = w.num_seqs
+    # calibrate on a few sequences, then size the sample to ~target_s
+    n = max(1, min(S, 4))
+    elapsed_total, bytes_total, seqs_total, reps = 0.0, 0, 0, 0
+    idx = 0
+    while elapsed_total < target_s and reps < 64:
+        sel = [(idx + i) % S for i in range(n)]
+        idx = (idx + n) % S
+        q = w.q[sel]
+        tb = w.block_tables[sel]
+        cl = w.context_lens[sel]
+        t0 = time.perf_counter()
+        oracle.paged_decode(q, w.k_cache, w.v_cache, tb, cl, w.scale, w.dtype)
+        dt = time.perf_counter() - t0
+        elapsed_total += dt
+        bytes_total += int(np.sum(cl.astype(np.int64))) * w.num_kv_heads * 2 * w.head_dim * w.elem_bytes
+        seqs_total += n
+        reps += 1
+        if dt > 0 and elapsed_total < target_s:
+            n = int(min(S, max(1, n * max(1.0, (target_s - elapsed_total) / dt / 2))))
+    return {
+        "value": bytes_total / elapsed_total / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "seq_layers_per_s": seqs_total / elapsed_total,
+        "seconds": round(elapsed_total, 3),
+        "sample": (f"{seqs_total} sequence-layers of the same workload (all {w.num_q_heads} q heads each, "
+                   f"{bytes_total / 1e9:.3f} GB of K/V), fp64 oracle, {threads} OpenMP threads, "
+                   f"host cores in affinity mask: {len(os.sched_getaffinity(0))}"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_405_amd import binding as B
+    from paged_kv_cache_405_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()                                                    # fail loudly if the library is missing
+
+    w = W.WORKLOADS[args.workload](poison=False)
+    layers = args.layers or (80 if w.num_q_heads == 64 else 32)
+    layout = B.PA_LAYOUT_BHTD if args.layout == "bhtd" else B.PA_LAYOUT_BTHD
+    pt = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    log(f"[bench] workload {w.name}: {w.description}; layers {layers}; partition {pt}; layout {args.layout}")
+
+    def dev_arr(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # layer 0 holds the seeded workload; the other layers get their own pools
+    # and queries from a seeded device generator (same shapes, same tables)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    ctx = torch.from_numpy(w.context_lens).to(dev)
+    slots = torch.from_numpy(w.slot_mapping).to(dev)
+    kc0 = B.to_layout(dev_arr(w.k_cache), layout)
+    cache_shape = tuple(kc0.shape)
+    Ls = []
+    for li in range(layers):
+        if li == 0:
+            kc, vc = kc0, B.to_layout(dev_arr(w.v_cache), layout)
+            q, nk, nv = dev_arr(w.q), dev_arr(w.new_k), dev_arr(w.new_v)
+        else:
+            kc = torch.randn(cache_shape, generator=gen, device=dev, dtype=tdt)
+            vc = torch.randn(cache_shape, generator=gen, device=dev, dtype=tdt)
+            q = torch.randn(tuple(w.q.shape), generator=gen, device=dev, dtype=tdt)
+            nk = torch.randn(tuple(w.new_k.shape), generator=gen, device=dev, dtype=tdt)
+            nv = torch.randn(tuple(w.new_v.shape), generator=gen, device=dev, dtype=tdt)
+        Ls.append((kc, vc, q, nk, nv, torch.empty_like(q)))
+    ws_bytes = B.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                           w.max_blocks_per_seq, {"f32": 0, "f16": 1, "bf16": 2}[w.dtype], pt)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    kv_per_layer = w.kv_bytes()
+    log(f"[bench] pools ready: {layers} x {2 * kc0.numel() * kc0.element_size() / 1e9:.2f} GB; "
+        f"KV bytes per decode call {kv_per_layer / 1e9:.4f} GB; workspace {ws_bytes} B")
+
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for li, (kc, vc, q, nk, nv, out) in enumerate(Ls):
+            B.pa_reshape_and_cache(nk, nv, kc, vc, slots, layout=layout, stream=stream)
+            if events is not None:
+                events[2 * li].record(stream)
+            B.pa_decode_ex(out, q, kc, vc, tables, ctx, w.scale, layout=layout, partition_tokens=pt,
+                           workspace=ws, stream=stream)
+            if events is not None:
+                events[2 * li + 1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * layers)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(ev[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    call_ms = [ev[k][2 * li].elapsed_time(ev[k][2 * li + 1]) for k in range(args.steps) for li in range(layers)]
+    avg_call_ms = statistics.fmean(call_ms)
+    log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms (wall {wall * 1e3:.3f} ms); "
+        f"decode call avg {avg_call_ms * 1e3:.2f} us, median {statistics.median(call_ms) * 1e3:.2f} us")
+
+    calls = args.steps * layers
+    kv_gbs = kv_per_layer * calls / (total_ms * 1e-3) / 1e9
+    achieved = kv_per_layer / (avg_call_ms * 1e-3) / 1e9
+    seq_layers = w.num_seqs * calls / (total_ms * 1e-3)
+    result = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal q/K/V, seeded block tables and context lengths)",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "layers": layers,
+            "partition_tokens": pt, "layout": args.layout, "sum_context_tokens": int(w.context_lens.sum()),
+            "parallelism": "single GPU",
+        },
+        "seq_layers_per_s": round(seq_layers, 1),
+        "hbm_peak_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_layer": kv_per_layer,
+        "roofline": {
+            "kernel": "pa_decode call (decode kernel + split-K reduce kernel when partitioned)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_call_us": round(avg_call_ms * 1e3, 3),
+            "bytes_per_call": kv_per_layer,
+        },
+        "append_and_decode_us_per_layer": round(total_ms * 1e3 / calls, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cw = W.WORKLOADS[args.workload](poison=False)
+        result["cpu_baseline"] = cpu_baseline(cw, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged decode attention library
+ * (libpa_mi355x.so).
+ *
+ * Two operations, both from the pages on vLLM's PagedAttention:
+ *
+ *   pa_decode            -- one decode step of attention for a batch of
+ *                           sequences whose K/V history is stored in
+ *                           fixed-size blocks scattered through a shared pool
+ *                           and reached through a per-sequence block table.
+ *                           Source: "vLLM 与 PagedAttention"
+ *                           (inference.mavenzero.com/case-studies/vllm),
+ *                           section 二, sub-sections "PagedAttention 的解法"
+ *                           (blocks of usually 16 tokens, logical-to-physical
+ *                           block table, shared pool) and "注意力计算改造"
+ *                           (K/V read block by block, per-block results
+ *                           accumulated; kernel sketch with q, key/value
+ *                           caches, block table, context length and block
+ *                           size as its arguments).
+ *   pa_reshape_and_cache -- append each new token's K and V rows into its
+ *                           slot of the pool.  Source: same page, "PagedAttention
+ *                           的解法" (a new block is taken only once the last
+ *                           one is full), and "指南" (illegalscreed.cn
+ *                           .../vllm/guide-line), section "为什么 vLLM 快：
+ *                           PagedAttention" (blocks allocated on demand,
+ *                           anywhere in the shared pool).
+ *
+ * Everything below is a plain C interface: device pointers, sizes, enums and
+ * an opaque stream.  No function allocates device memory.
+ *
+ * Common conventions
+ *   - Device pointers are owned by the caller and must stay valid until the
+ *     work enqueued on `stream` has finished.  The library keeps no pointer
+ *     after a call returns and has no global mutable state; calls are
+ *     re-entrant and may run concurrently on different streams.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work; they never synchronise.
+ *   - Every argument check runs on the host before any HIP call.  A return
+ *     other than PA_OK means nothing was enqueued.  PA_ERR_HIP reports a
+ *     failed launch (for example: no GPU); device faults surface at the
+ *     caller's next synchronisation, as for any HIP kernel.
+ *   - Elements are stored as `dtype`; all arithmetic is fp32.
+ *   - 16-byte alignment is required for q, out, k, v, k_cache, v_cache and
+ *     workspace (the kernels move 16-byte vectors); 4-byte alignment for the
+ *     int32 arrays and 8-byte for slot_mapping.
+ */
+#ifndef PA_MI355X_PA_H_
+#define PA_MI355X_PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, Hq % Hkv != 0,
+                                 non-finite scale, partition not a multiple of block_size */
+    PA_ERR_UNSUPPORTED = 2,   /* head_dim, block_size, dtype or layout outside the supported set */
+    PA_ERR_WORKSPACE = 3,     /* split-K needs a workspace and the one given is missing or too small */
+    PA_ERR_HIP = 4            /* a HIP launch failed */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_F32 = 0,
+    PA_F16 = 1,
+    PA_BF16 = 2
+} pa_dtype;
+
+/*
+ * Cache layouts.  Both caches (K and V) use the same one.
+ *   PA_LAYOUT_BHTD: [num_blocks, num_kv_heads, block_size, head_dim].  Each
+ *                   (block, kv head) tile is one contiguous run of
+ *                   block_size*head_dim elements.  Default.
+ *   PA_LAYOUT_BTHD: [num_blocks, block_size, num_kv_heads, head_dim], the
+ *                   layout of the kernel sketch on "vLLM 与 PagedAttention",
+ *                   sub-section "注意力计算改造".
+ */
+typedef enum pa_layout {
+    PA_LAYOUT_BHTD = 0,
+    PA_LAYOUT_BTHD = 1
+} pa_layout;
+
+/* Supported shapes: head_dim in {32, 64, 128, 256}; block_size in {8, 16, 32};
+ * any num_q_heads that is a multiple of num_kv_heads. */
+
+/*
+ * pa_decode -- paged decode attention, one query token per sequence.
+ *
+ *   out[s, h, :] = softmax_t( scale * q[s, h, :] . K[s, t, g, :] ) V[s, t, g, :]
+ *
+ * over the tokens t = 0 .. context_lens[s]-1 of sequence s, where token t
+ * lives in physical block block_tables[s, t / block_size] at offset
+ * t % block_size, and q head h reads kv head g = h / (num_q_heads/num_kv_heads).
+ *
+ *   out            [num_seqs, num_q_heads, head_dim]  dtype, written in full
+ *   q              [num_seqs, num_q_heads, head_dim]  dtype
+ *   k_cache,
+ *   v_cache        pool in PA_LAYOUT_BHTD, dtype, read only
+ *   block_tables   [num_seqs, max_blocks_per_seq] int32, row-major; only the
+ *                  first ceil(context_lens[s]/block_size) entries of row s are
+ *                  read and each must be a valid physical block
+ *   context_lens   [num_seqs] int32, every cached token of the sequence (the
+ *                  token appended this step included); 0 gives a zero row;
+ *                  values above max_blocks_per_seq*block_size are clamped
+ *   scale          finite fp32 factor on q.k (usually 1/sqrt(head_dim))
+ *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
+ *                  bytes for split-K partials (may be NULL when that is 0);
+ *                  its content on entry does not matter
+ *
+ * Equivalent to pa_decode_ex with num_blocks = INT32_MAX (table entries are
+ * trusted), layout PA_LAYOUT_BHTD and partition_tokens = 0.
+ */
+pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens,
+                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                    int block_size, int max_blocks_per_seq, float scale, pa_dtype dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_ex -- pa_decode with the pool size, the cache layout and the
+ * split-K partition made explicit.
+ *
+ *   num_blocks        blocks in the pool; a table entry outside [0, num_blocks)
+ *                     contributes no tokens instead of being read
+ *   layout            PA_LAYOUT_BHTD or PA_LAYOUT_BTHD
+ *   partition_tokens  0  = the library picks (split-K for long contexts);
+ *                     -1 = single pass, one workgroup reads a whole context;
+ *                     N > 0 = each workgroup reads at most N tokens of one
+ *                     sequence (N a multiple of block_size) and a reduce kernel
+ *                     merges the partitions' (max, sum, partial output).
+ *
+ * Per-block partial results are combined with a running max and sum
+ * ("online softmax"); the combine across partitions is the same operation.
+ */
+pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                       pa_dtype dtype, pa_layout layout, int partition_tokens,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_workspace_bytes -- bytes of workspace pa_decode / pa_decode_ex
+ * need for these sizes and this partition_tokens (0, -1 or N, as above).
+ * Writes 0 when the call runs single pass.  Returns the same status the
+ * decode call would return for these sizes.
+ */
+pa_status pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int max_blocks_per_seq, pa_dtype dtype,
+                                    int partition_tokens, size_t *bytes_out);
+
+/*
+ * pa_reshape_and_cache -- append new K/V rows into the pool.
+ *
+ *   k, v           [num_tokens, num_kv_heads, head_dim] dtype, contiguous
+ *   k_cache,
+ *   v_cache        pool in `layout`, [num_blocks, ...] as above
+ *   slot_mapping   [num_tokens] int64; token i goes to physical block
+ *                  slot / block_size at offset slot % block_size; a negative
+ *                  slot skips the token, a slot >= num_blocks*block_size is
+ *                  skipped as well (never written)
+ *
+ * Elements are copied bit for bit.  Two tokens with the same slot: one of
+ * them wins, which one is unspecified.
+ */
+pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_cache,
+                               const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
+                               int head_dim, int block_size, int num_blocks, pa_dtype dtype,
+                               pa_layout layout, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *pa_status_string(pa_status status);
+
+/* Version of this interface (major * 100 + minor). */
+int pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_MI355X_PA_H_ */

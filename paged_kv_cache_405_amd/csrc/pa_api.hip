@@ -1,0 +1,251 @@
+// pa_api.hip -- the C ABI declared in include/pa.h: host-side argument
+// checks, the launch plan (split-K partition, q-head grouping, workspace
+// carving) and the kernel launches on the caller's stream.
+//
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and touches no device state.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr size_t WS_ALIGN = 256;
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool supported_head_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+bool supported_block_size(int b) { return b == 8 || b == 16 || b == 32; }
+bool supported_dtype(pa_dtype t) { return t == PA_F32 || t == PA_F16 || t == PA_BF16; }
+bool supported_layout(pa_layout l) { return l == PA_LAYOUT_BHTD || l == PA_LAYOUT_BTHD; }
+
+struct Plan {
+    int partition_blocks = 0;   // blocks per partition
+    int max_partitions = 1;     // grid x extent
+    int gt = 1;                 // q heads per workgroup
+    int group_split = 1;        // workgroups per kv head
+    size_t ml_bytes = 0;        // (max, sum) pairs, first in the workspace
+    size_t ws_bytes = 0;        // total workspace (0 = single pass)
+};
+
+// Partition length the library picks when the caller passes 0: contexts that
+// can exceed 512 tokens are cut into 512-token partitions so that long and
+// ragged batches spread over many workgroups.
+int auto_partition_tokens(int block_size, int max_blocks)
+{
+    const long long max_tokens = (long long)block_size * max_blocks;
+    return max_tokens > 512 ? 512 : -1;
+}
+
+pa_status check_sizes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int max_blocks_per_seq, pa_dtype dtype, int partition_tokens)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (num_q_heads % num_kv_heads != 0)
+        return PA_ERR_INVALID_ARG;
+    if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % block_size != 0))
+        return PA_ERR_INVALID_ARG;
+    if ((long long)max_blocks_per_seq * block_size > (1LL << 30))
+        return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+pa_status make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                    int max_blocks_per_seq, pa_dtype dtype, int partition_tokens, Plan *pl)
+{
+    pa_status st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               max_blocks_per_seq, dtype, partition_tokens);
+    if (st != PA_OK)
+        return st;
+    int pt = partition_tokens == 0 ? auto_partition_tokens(block_size, max_blocks_per_seq) : partition_tokens;
+    const long long max_tokens = (long long)block_size * max_blocks_per_seq;
+    if (pt < 0 || pt >= max_tokens) {
+        pl->partition_blocks = max_blocks_per_seq;
+        pl->max_partitions = 1;
+    } else {
+        pl->partition_blocks = pt / block_size;
+        pl->max_partitions = (max_blocks_per_seq + pl->partition_blocks - 1) / pl->partition_blocks;
+    }
+    const int group = num_q_heads / num_kv_heads;
+    pl->gt = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    pl->group_split = group / pl->gt;
+    if ((long long)num_kv_heads * pl->group_split > 65535 || num_seqs > 65535)
+        return PA_ERR_UNSUPPORTED;
+    if (pl->max_partitions > 1) {
+        const size_t units = (size_t)num_seqs * num_q_heads * pl->max_partitions;
+        pl->ml_bytes = round_up(units * sizeof(float2), WS_ALIGN);
+        pl->ws_bytes = pl->ml_bytes + units * (size_t)head_dim * sizeof(float);
+    } else {
+        pl->ml_bytes = 0;
+        pl->ws_bytes = 0;
+    }
+    return PA_OK;
+}
+
+void layout_strides(pa_layout layout, int num_kv_heads, int block_size, int head_dim,
+                    int64_t *block_stride, int64_t *head_stride, int64_t *token_stride)
+{
+    *block_stride = (int64_t)num_kv_heads * block_size * head_dim;
+    if (layout == PA_LAYOUT_BHTD) {
+        *head_stride = (int64_t)block_size * head_dim;
+        *token_stride = head_dim;
+    } else {
+        *head_stride = head_dim;
+        *token_stride = (int64_t)num_kv_heads * head_dim;
+    }
+}
+
+int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int max_blocks_per_seq, pa_dtype dtype,
+                                    int partition_tokens, size_t *bytes_out)
+{
+    if (!bytes_out)
+        return PA_ERR_INVALID_ARG;
+    Plan pl;
+    pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, dtype, partition_tokens, &pl);
+    *bytes_out = st == PA_OK ? pl.ws_bytes : 0;
+    return st;
+}
+
+pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                       pa_dtype dtype, pa_layout layout, int partition_tokens,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    Plan pl;
+    pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, dtype, partition_tokens, &pl);
+    if (st != PA_OK)
+        return st;
+    if (!supported_layout(layout))
+        return PA_ERR_UNSUPPORTED;
+    if (num_blocks <= 0 || !std::isfinite(scale))
+        return PA_ERR_INVALID_ARG;
+    if (num_seqs == 0)
+        return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return PA_ERR_INVALID_ARG;
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned(workspace, 16)))
+        return PA_ERR_WORKSPACE;
+
+    pa::DecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.out = out;
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.tables = block_tables;
+    p.ctx = context_lens;
+    if (pl.ws_bytes > 0) {
+        p.ws_ml = reinterpret_cast<float2 *>(workspace);
+        p.ws_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ml_bytes);
+    }
+    layout_strides(layout, num_kv_heads, block_size, head_dim, &p.block_stride, &p.head_stride, &p.token_stride);
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.partition_blocks = pl.partition_blocks;
+    p.max_partitions = pl.max_partitions;
+    p.group = num_q_heads / num_kv_heads;
+    p.group_split = pl.group_split;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (dtype) {
+    case PA_F32: e = pa::launch_decode_f32(p, head_dim, block_size, pl.gt, s); break;
+    case PA_F16: e = pa::launch_decode_f16(p, head_dim, block_size, pl.gt, s); break;
+    default: e = pa::launch_decode_bf16(p, head_dim, block_size, pl.gt, s); break;
+    }
+    if (e != hipSuccess)
+        return PA_ERR_HIP;
+    if (pl.max_partitions > 1) {
+        e = pa::launch_reduce(p, (int)dtype, head_dim, block_size, s);
+        if (e != hipSuccess)
+            return PA_ERR_HIP;
+    }
+    return PA_OK;
+}
+
+pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens,
+                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                    int block_size, int max_blocks_per_seq, float scale, pa_dtype dtype,
+                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    return pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, INT32_MAX, scale, dtype,
+                        PA_LAYOUT_BHTD, 0, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_cache,
+                               const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
+                               int head_dim, int block_size, int num_blocks, pa_dtype dtype,
+                               pa_layout layout, void *stream)
+{
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size) ||
+        !supported_layout(layout))
+        return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0)
+        return PA_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(slot_mapping, 8))
+        return PA_ERR_INVALID_ARG;
+
+    pa::AppendParams a;
+    std::memset(&a, 0, sizeof(a));
+    a.k = k;
+    a.v = v;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.slots = slot_mapping;
+    layout_strides(layout, num_kv_heads, block_size, head_dim, &a.block_stride, &a.head_stride, &a.token_stride);
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.num_slots = (int64_t)num_blocks * block_size;
+    a.elem_bytes = elem_bytes(dtype);
+    a.chunks_per_head = head_dim * a.elem_bytes / 16;
+    return pa::launch_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+const char *pa_status_string(pa_status status)
+{
+    switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape, element type or layout";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int pa_abi_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,13 @@
+// pa_decode_bf16.hip -- instantiates the vector-path decode kernels for bf16
+// storage (one translation unit per element type keeps builds parallel).
+#include "pa_decode_vec.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+hipError_t launch_decode_bf16(const DecodeParams &p, int head_dim, int block_size, int gt, hipStream_t st)
+{
+    return launch_decode_dtype<bf16_t>(p, head_dim, block_size, gt, st);
+}
+
+}  // namespace pa

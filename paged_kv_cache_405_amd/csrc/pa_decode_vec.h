@@ -1,0 +1,366 @@
+// pa_decode_vec.h -- paged decode attention, vector (VALU) path for gfx950.
+//
+// Method: "vLLM 与 PagedAttention" (inference.mavenzero.com/case-studies/vllm),
+// section 二: the context of a sequence is stored in fixed-size blocks of a
+// shared pool that a per-sequence block table maps (sub-section
+// "PagedAttention 的解法"); attention reads K/V one block at a time and
+// accumulates the per-block results (sub-section "注意力计算改造").  The
+// accumulation is done as an online softmax: a running max m, a running sum
+// l and an unnormalised output acc, rescaled by exp(m_old - m_new) whenever
+// the max grows.  Partitions of one context (split-K) are merged the same way.
+//
+// Work decomposition (one workgroup per (partition, kv-head group, sequence)):
+//   - a wave reads a whole (block, kv head) tile of K and of V with 16-byte
+//     loads: lane -> (token row, 16-byte chunk of head_dim); LPT lanes cover
+//     one token's row, so a wave-wide load covers TPL = 64/LPT tokens;
+//   - q.k is a per-lane dot over the lane's chunk followed by a DPP sum over
+//     the LPT lanes of the row (no LDS);
+//   - each token row keeps its own (m, l, acc) over the tokens it sees; the
+//     rows are merged with cross-lane shuffles after the block loop, and the
+//     waves of the workgroup through LDS;
+//   - the waves of a workgroup take the partition's blocks round robin, and
+//     each wave issues the next block's loads before it computes the current
+//     one (register double buffering), so two blocks per wave are in flight.
+//   - GT q heads that share one kv head (grouped-query attention) are handled
+//     by one workgroup, so each K/V element is read once per GT heads.
+//
+// Scores are kept in log2 units (scale * log2(e) folded into one factor) so
+// that exponentials are single v_exp_f32 instructions.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+template <typename T, int D, int BS, int GT, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams P)
+{
+    using V = Vec<T>;
+    constexpr int VEC = V::N;                 // elements per 16 bytes
+    constexpr int ES = 16 / VEC;              // element bytes
+    constexpr int LPT = D / VEC;              // lanes per token row
+    static_assert(LPT >= 1 && LPT <= 64 && (64 % LPT) == 0, "head_dim / dtype combination");
+    constexpr int TPL = 64 / LPT;             // token rows per wave-wide load
+    constexpr int ROWS = TPL < BS ? TPL : BS; // rows that carry tokens
+    constexpr bool ALL_ROWS = TPL <= BS;
+    constexpr int NLD_TILE = BS / ROWS;       // wave-wide loads per (block, kv head) tile
+    constexpr int NLD = NLD_TILE < 4 ? NLD_TILE : 4;   // loads per step (a slab of the tile)
+    constexpr int NSLAB = NLD_TILE / NLD;     // steps per tile
+    constexpr int SLAB_TOK = NLD * ROWS;      // tokens per step
+
+    const int p = blockIdx.x;
+    const int hg = blockIdx.y;
+    const int s = blockIdx.z;
+
+    int ctx = P.ctx[s];
+    const int cap = P.max_blocks * BS;
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    const int nblk = (ctx + BS - 1) / BS;
+    const int npart = nblk == 0 ? 1 : (nblk + P.partition_blocks - 1) / P.partition_blocks;
+    if (p >= npart)
+        return;
+
+    const int kvh = hg / P.group_split;
+    const int qh0 = kvh * P.group + (hg - kvh * P.group_split) * GT;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = lane / LPT;
+    const int chunk = lane % LPT;
+    const bool row_on = ALL_ROWS || row < ROWS;
+    const int row_c = row_on ? row : 0;
+
+    float qf[GT][VEC];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        const int64_t qi = ((int64_t)s * P.num_q_heads + qh0 + g) * D + chunk * VEC;
+        V::widen(ld16(static_cast<const char *>(P.q) + qi * ES), qf[g]);
+    }
+
+    float m[GT], l[GT], acc[GT][VEC];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        m[g] = NEG_BIG;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            acc[g][e] = 0.f;
+    }
+
+    const int64_t lane_off = ((int64_t)kvh * P.head_stride + (int64_t)row_c * P.token_stride + chunk * VEC) * ES;
+    const char *kb = static_cast<const char *>(P.k) + lane_off;
+    const char *vb = static_cast<const char *>(P.v) + lane_off;
+    const int64_t blk_bytes = P.block_stride * ES;
+    const int64_t ld_bytes = (int64_t)ROWS * P.token_stride * ES;
+    const int32_t *trow = P.tables + (int64_t)s * P.max_blocks;
+
+    const int b0 = p * P.partition_blocks;
+    const int b1 = min(nblk, b0 + P.partition_blocks);
+    const int q1 = (b1 - b0) * NSLAB;         // steps in this partition
+
+    // one step = NLD wave-wide loads of K and of V (a slab of one tile)
+    auto load_step = [&](int q, uint4 *kd, uint4 *vd) {
+        const int j = b0 + q / NSLAB;
+        const int sl = q % NSLAB;
+        const int phys = trow[j];
+        const bool ok = (unsigned)phys < (unsigned)P.num_blocks;
+        const int64_t boff = (int64_t)(ok ? phys : 0) * blk_bytes + (int64_t)sl * NLD * ld_bytes;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            kd[i] = ld16(kb + boff + i * ld_bytes);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            vd[i] = ld16(vb + boff + i * ld_bytes);
+        return ok;
+    };
+
+    uint4 kr[NLD], vr[NLD], kn[NLD], vn[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+        kn[i] = vn[i] = make_uint4(0u, 0u, 0u, 0u);
+    int q = wave;
+    bool ok_cur = false;
+    if (q < q1)
+        ok_cur = load_step(q, kr, vr);
+
+    for (; q < q1; q += NW) {
+        bool ok_next = false;
+        if (q + NW < q1)
+            ok_next = load_step(q + NW, kn, vn);
+        const int t0 = (b0 + q / NSLAB) * BS + (q % NSLAB) * SLAB_TOK;   // first token of the step
+
+        // scores of this step, log2 units
+        float sc[GT][NLD];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            float kf[VEC];
+            V::widen(kr[i], kf);
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    d = fmaf(qf[g][e], kf[e], d);
+                sc[g][i] = group_sum<LPT>(d) * P.scale_log2;
+            }
+        }
+        float vf[NLD][VEC];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            V::widen(vr[i], vf[i]);
+
+        // tokens past the context, of an unmapped block, or of an idle row:
+        // select (never multiply) so that whatever the memory holds is ignored
+        const bool full = ok_cur && t0 + SLAB_TOK <= ctx && ALL_ROWS;
+        if (!full) {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int t = t0 + i * ROWS + row;
+                const bool valid = ok_cur && row_on && t < ctx;
+                if (!valid) {
+#pragma unroll
+                    for (int g = 0; g < GT; ++g)
+                        sc[g][i] = -INFINITY;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        vf[i][e] = 0.f;
+                }
+            }
+        }
+
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            float mx = sc[g][0];
+#pragma unroll
+            for (int i = 1; i < NLD; ++i)
+                mx = fmaxf(mx, sc[g][i]);
+            const float mn = fmaxf(m[g], mx);
+            const float alpha = fast_exp2(m[g] - mn);
+            float pr[NLD];
+            float ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                pr[i] = fast_exp2(sc[g][i] - mn);
+                ps += pr[i];
+            }
+            l[g] = fmaf(l[g], alpha, ps);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float a = acc[g][e] * alpha;
+#pragma unroll
+                for (int i = 0; i < NLD; ++i)
+                    a = fmaf(pr[i], vf[i][e], a);
+                acc[g][e] = a;
+            }
+            m[g] = mn;
+        }
+
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            kr[i] = kn[i];
+            vr[i] = vn[i];
+        }
+        ok_cur = ok_next;
+    }
+
+    // merge the token rows of the wave (lanes that differ in the row bits)
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            const float mo = __shfl_xor(m[g], off);
+            const float lo = __shfl_xor(l[g], off);
+            const float mn = fmaxf(m[g], mo);
+            const float a = fast_exp2(m[g] - mn);
+            const float b = fast_exp2(mo - mn);
+            l[g] = l[g] * a + lo * b;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                acc[g][e] = acc[g][e] * a + __shfl_xor(acc[g][e], off) * b;
+            m[g] = mn;
+        }
+    }
+
+    const bool single = npart == 1;
+    auto emit = [&](int g, int d, float M, float L, float A) {
+        const int qh = qh0 + g;
+        const int64_t sh = (int64_t)s * P.num_q_heads + qh;
+        if (single) {
+            Store<T>::one(P.out, sh * D + d, L > 0.f ? A / L : 0.f);
+        } else {
+            P.ws_acc[(sh * P.max_partitions + p) * D + d] = A;
+            if (d == 0)
+                P.ws_ml[sh * P.max_partitions + p] = make_float2(M, L);
+        }
+    };
+
+    if constexpr (NW == 1) {
+        if (row == 0) {
+#pragma unroll
+            for (int g = 0; g < GT; ++g)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    emit(g, chunk * VEC + e, m[g], l[g], acc[g][e]);
+        }
+    } else {
+        __shared__ float sm_m[NW][GT], sm_l[NW][GT];
+        __shared__ float sm_acc[NW][GT][D];
+        if (row == 0) {
+#pragma unroll
+            for (int g = 0; g < GT; ++g)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    sm_acc[wave][g][chunk * VEC + e] = acc[g][e];
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                sm_m[wave][g] = m[g];
+                sm_l[wave][g] = l[g];
+            }
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < GT * D; idx += NW * 64) {
+            const int g = idx / D;
+            const int d = idx - g * D;
+            float M = sm_m[0][g];
+#pragma unroll
+            for (int w = 1; w < NW; ++w)
+                M = fmaxf(M, sm_m[w][g]);
+            float L = 0.f, A = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float c = fast_exp2(sm_m[w][g] - M);
+                L = fmaf(sm_l[w][g], c, L);
+                A = fmaf(sm_acc[w][g][d], c, A);
+            }
+            emit(g, d, M, L, A);
+        }
+    }
+}
+
+// Split-K reduce: one wave per (q head, sequence) merges the partitions'
+// (max, sum, unnormalised output) and writes the normalised output.
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(64) void reduce_kernel(const DecodeParams P)
+{
+    const int qh = blockIdx.x;
+    const int s = blockIdx.y;
+    int ctx = P.ctx[s];
+    const int cap = P.max_blocks * BS;
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    const int nblk = (ctx + BS - 1) / BS;
+    const int npart = nblk == 0 ? 1 : (nblk + P.partition_blocks - 1) / P.partition_blocks;
+    if (npart <= 1)
+        return;
+    const int lane = threadIdx.x;
+    const int64_t sh = (int64_t)s * P.num_q_heads + qh;
+    const float2 *ml = P.ws_ml + sh * P.max_partitions;
+    const float *acc = P.ws_acc + sh * P.max_partitions * D;
+
+    float M = NEG_BIG;
+    for (int i = lane; i < npart; i += 64)
+        M = fmaxf(M, ml[i].x);
+    M = group_max<64>(M);
+    float L = 0.f;
+    for (int i = lane; i < npart; i += 64) {
+        const float2 v = ml[i];
+        L = fmaf(v.y, fast_exp2(v.x - M), L);
+    }
+    L = group_sum<64>(L);
+    for (int d = lane; d < D; d += 64) {
+        float A = 0.f;
+        for (int i = 0; i < npart; ++i)
+            A = fmaf(acc[(int64_t)i * D + d], fast_exp2(ml[i].x - M), A);
+        Store<T>::one(P.out, sh * D + d, L > 0.f ? A / L : 0.f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host-side dispatch over the compile-time shape
+// ---------------------------------------------------------------------------
+constexpr int DECODE_WAVES = 4;
+
+template <typename T, int D, int BS, int GT>
+hipError_t launch_decode_shape(const DecodeParams &p, hipStream_t st)
+{
+    dim3 grid(p.max_partitions, p.num_kv_heads * p.group_split, p.num_seqs);
+    hipLaunchKernelGGL((decode_vec_kernel<T, D, BS, GT, DECODE_WAVES>), grid, dim3(DECODE_WAVES * 64), 0, st, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int BS>
+hipError_t launch_decode_gt(const DecodeParams &p, int gt, hipStream_t st)
+{
+    switch (gt) {
+    case 1: return launch_decode_shape<T, D, BS, 1>(p, st);
+    case 2: return launch_decode_shape<T, D, BS, 2>(p, st);
+    case 4: return launch_decode_shape<T, D, BS, 4>(p, st);
+    case 8: return launch_decode_shape<T, D, BS, 8>(p, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_decode_bs(const DecodeParams &p, int bs, int gt, hipStream_t st)
+{
+    switch (bs) {
+    case 8: return launch_decode_gt<T, D, 8>(p, gt, st);
+    case 16: return launch_decode_gt<T, D, 16>(p, gt, st);
+    case 32: return launch_decode_gt<T, D, 32>(p, gt, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_decode_dtype(const DecodeParams &p, int head_dim, int bs, int gt, hipStream_t st)
+{
+    switch (head_dim) {
+    case 32: return launch_decode_bs<T, 32>(p, bs, gt, st);
+    case 64: return launch_decode_bs<T, 64>(p, bs, gt, st);
+    case 128: return launch_decode_bs<T, 128>(p, bs, gt, st);
+    case 256: return launch_decode_bs<T, 256>(p, bs, gt, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pa

@@ -1,0 +1,187 @@
+// pa_device.h -- device helpers shared by the gfx950 kernels of the library:
+// storage types, 16-byte vector moves, wave64 reductions, the launch
+// parameter blocks.  Written for CDNA4 (wave64, DPP within 16-lane rows).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// ---------------------------------------------------------------------------
+// storage types: fp32, fp16 and bf16 (bf16 handled as raw 16-bit patterns)
+// ---------------------------------------------------------------------------
+struct f32_t { using storage = float; };
+struct f16_t { using storage = uint16_t; };
+struct bf16_t { using storage = uint16_t; };
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Widen the 16 bytes of one uint4 into VEC fp32 values (VEC = 16 / sizeof).
+template <typename T> struct Vec;
+
+template <> struct Vec<f32_t> {
+    static constexpr int N = 4;
+    __device__ __forceinline__ static void widen(const uint4 &u, float *f) {
+        f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+        f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+    }
+    __device__ __forceinline__ static void store(void *p, const float *f) {
+        *reinterpret_cast<float *>(p) = f[0];
+        reinterpret_cast<float *>(p)[1] = f[1];
+        reinterpret_cast<float *>(p)[2] = f[2];
+        reinterpret_cast<float *>(p)[3] = f[3];
+    }
+};
+
+template <> struct Vec<f16_t> {
+    static constexpr int N = 8;
+    __device__ __forceinline__ static void widen2(uint32_t w, float &a, float &b) {
+        half2v h = __builtin_bit_cast(half2v, w);
+        a = (float)h.x; b = (float)h.y;
+    }
+    __device__ __forceinline__ static void widen(const uint4 &u, float *f) {
+        widen2(u.x, f[0], f[1]); widen2(u.y, f[2], f[3]);
+        widen2(u.z, f[4], f[5]); widen2(u.w, f[6], f[7]);
+    }
+};
+
+template <> struct Vec<bf16_t> {
+    static constexpr int N = 8;
+    __device__ __forceinline__ static void widen2(uint32_t w, float &a, float &b) {
+        a = __uint_as_float(w << 16);
+        b = __uint_as_float(w & 0xffff0000u);
+    }
+    __device__ __forceinline__ static void widen(const uint4 &u, float *f) {
+        widen2(u.x, f[0], f[1]); widen2(u.y, f[2], f[3]);
+        widen2(u.z, f[4], f[5]); widen2(u.w, f[6], f[7]);
+    }
+};
+
+// fp32 -> storage, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    _Float16 h = (_Float16)x;                 // v_cvt_f16_f32, RNE
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u)      // NaN: keep it a (quiet) NaN
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Store;
+template <> struct Store<f32_t> {
+    __device__ __forceinline__ static void one(void *base, int64_t i, float x) {
+        reinterpret_cast<float *>(base)[i] = x;
+    }
+};
+template <> struct Store<f16_t> {
+    __device__ __forceinline__ static void one(void *base, int64_t i, float x) {
+        reinterpret_cast<uint16_t *>(base)[i] = f32_to_f16_bits(x);
+    }
+};
+template <> struct Store<bf16_t> {
+    __device__ __forceinline__ static void one(void *base, int64_t i, float x) {
+        reinterpret_cast<uint16_t *>(base)[i] = f32_to_bf16_bits(x);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// 16-byte global moves
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 ld16(const void *p) {
+    return *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ void st16(void *p, const uint4 &v) {
+    *reinterpret_cast<uint4 *>(p) = v;
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions.  Within a 16-lane row: DPP (quad_perm xor 1 and xor 2,
+// then half-row and row mirrors, which pair lanes whose partial results are
+// already equal within their quad / half row).  Across rows: ds_bpermute.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int DPP_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_HMIRROR = 0x141; // row_half_mirror
+constexpr int DPP_MIRROR = 0x140;  // row_mirror
+
+// Sum over aligned groups of W lanes (W = 1, 2, 4, 8, 16, 32, 64); every
+// lane of a group receives the group's sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (W >= 2) x += dpp<DPP_XOR1>(x);
+    if constexpr (W >= 4) x += dpp<DPP_XOR2>(x);
+    if constexpr (W >= 8) x += dpp<DPP_HMIRROR>(x);
+    if constexpr (W >= 16) x += dpp<DPP_MIRROR>(x);
+    if constexpr (W >= 32) x += __shfl_xor(x, 16);
+    if constexpr (W >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float x) {
+    if constexpr (W >= 2) x = fmaxf(x, dpp<DPP_XOR1>(x));
+    if constexpr (W >= 4) x = fmaxf(x, dpp<DPP_XOR2>(x));
+    if constexpr (W >= 8) x = fmaxf(x, dpp<DPP_HMIRROR>(x));
+    if constexpr (W >= 16) x = fmaxf(x, dpp<DPP_MIRROR>(x));
+    if constexpr (W >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+    if constexpr (W >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Finite stand-in for -infinity as the running max: exp2(m_old - m_new)
+// stays well defined (1 when both are the stand-in, 0 against a real score).
+constexpr float NEG_BIG = -1.0e30f;
+
+// ---------------------------------------------------------------------------
+// launch parameters
+// ---------------------------------------------------------------------------
+struct DecodeParams {
+    void *out;
+    const void *q;
+    const void *k;
+    const void *v;
+    const int32_t *tables;
+    const int32_t *ctx;
+    float *ws_acc;            // [S, Hq, P, D] unnormalised partial outputs
+    float2 *ws_ml;            // [S, Hq, P] (running max in log2 units, sum)
+    int64_t block_stride;     // elements between physical blocks
+    int64_t head_stride;      // elements between kv heads inside a block
+    int64_t token_stride;     // elements between tokens inside a block
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int max_blocks;           // table row length
+    int num_blocks;           // pool size (entries outside [0, num_blocks) contribute nothing)
+    int partition_blocks;     // blocks per split-K partition
+    int max_partitions;       // P (grid x extent)
+    int group;                // q heads per kv head
+    int group_split;          // workgroups sharing one kv head (each takes group/group_split q heads)
+    float scale_log2;         // scale * log2(e)
+};
+
+struct AppendParams {
+    const void *k;
+    const void *v;
+    void *k_cache;
+    void *v_cache;
+    const int64_t *slots;
+    int64_t block_stride, head_stride, token_stride;   // elements
+    int num_tokens;
+    int num_kv_heads;
+    int block_size;
+    int64_t num_slots;        // num_blocks * block_size
+    int chunks_per_head;      // head_dim * elem_bytes / 16
+    int elem_bytes;
+};
+
+}  // namespace pa

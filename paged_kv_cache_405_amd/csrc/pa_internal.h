@@ -1,0 +1,22 @@
+// pa_internal.h -- launchers shared between the C ABI (pa_api.cpp) and the
+// kernel translation units.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_device.h"
+
+namespace pa {
+
+enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// Vector-path decode (any q-head group size; `gt` q heads per workgroup) and
+// the split-K reduce.  Each returns hipSuccess or the launch error.
+hipError_t launch_decode_f32(const DecodeParams &p, int head_dim, int block_size, int gt, hipStream_t st);
+hipError_t launch_decode_f16(const DecodeParams &p, int head_dim, int block_size, int gt, hipStream_t st);
+hipError_t launch_decode_bf16(const DecodeParams &p, int head_dim, int block_size, int gt, hipStream_t st);
+hipError_t launch_reduce(const DecodeParams &p, int dtype, int head_dim, int block_size, hipStream_t st);
+hipError_t launch_append(const AppendParams &p, hipStream_t st);
+
+}  // namespace pa

@@ -1,0 +1,122 @@
+"""Shared test harness: move a seeded workload to the GPU, run the library
+through its C ABI, run the CPU oracle on the same arrays, compare.
+
+The oracle side only ever sees the generator's arrays; nothing computed by
+the GPU path feeds it.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from paged_kv_cache_405_amd import binding as B
+from paged_kv_cache_405_amd.workloads import Workload
+
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+# max-abs and relative-L2 bounds, against the oracle rounded to the output type
+TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-3), "bf16": (2e-3, 1e-3)}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.to(device)
+
+
+def to_host_storage(t: torch.Tensor, dtype: str) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+@dataclasses.dataclass
+class GpuInputs:
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    tables: torch.Tensor
+    ctx: torch.Tensor
+    new_k: torch.Tensor | None
+    new_v: torch.Tensor | None
+    slots: torch.Tensor | None
+    layout: int
+
+
+def upload(w: Workload, layout=B.PA_LAYOUT_BHTD) -> GpuInputs:
+    kc = B.to_layout(to_dev(w.k_cache, w.dtype), layout)
+    vc = B.to_layout(to_dev(w.v_cache, w.dtype), layout)
+    return GpuInputs(
+        q=to_dev(w.q, w.dtype), k_cache=kc, v_cache=vc,
+        tables=torch.from_numpy(w.block_tables).cuda(), ctx=torch.from_numpy(w.context_lens).cuda(),
+        new_k=None if w.new_k is None else to_dev(w.new_k, w.dtype),
+        new_v=None if w.new_v is None else to_dev(w.new_v, w.dtype),
+        slots=None if w.slot_mapping is None else torch.from_numpy(w.slot_mapping).cuda(),
+        layout=layout)
+
+
+def gpu_step(w: Workload, g: GpuInputs, partition_tokens=0, append=True, num_blocks=None) -> torch.Tensor:
+    """Append (if the workload has new tokens) then decode, on the current stream."""
+    if append and g.slots is not None:
+        B.pa_reshape_and_cache(g.new_k, g.new_v, g.k_cache, g.v_cache, g.slots, layout=g.layout)
+    out = torch.empty_like(g.q)
+    B.pa_decode_ex(out, g.q, g.k_cache, g.v_cache, g.tables, g.ctx, w.scale, layout=g.layout,
+                   partition_tokens=partition_tokens, num_blocks=num_blocks)
+    return out
+
+
+def oracle_step(w: Workload, append=True, context_lens=None) -> np.ndarray:
+    """The oracle's answer (float64) for append-then-decode on the workload's arrays."""
+    kc, vc = w.k_cache, w.v_cache
+    if append and w.slot_mapping is not None:
+        kc, vc = kc.copy(), vc.copy()
+        oracle.reshape_and_cache(w.new_k, w.new_v, kc, vc, w.slot_mapping, w.dtype)
+    ctx = w.context_lens if context_lens is None else context_lens
+    return oracle.paged_decode(w.q, kc, vc, w.block_tables, ctx, w.scale, w.dtype)
+
+
+@dataclasses.dataclass
+class Report:
+    max_abs: float
+    rel_l2: float
+    max_abs_unrounded: float
+    rel_l2_unrounded: float
+    worst_seq_rel_l2: float
+
+    def __str__(self):
+        return (f"max_abs {self.max_abs:.3e} rel_l2 {self.rel_l2:.3e} (vs unrounded: {self.max_abs_unrounded:.3e} / "
+                f"{self.rel_l2_unrounded:.3e}); worst per-seq rel_l2 {self.worst_seq_rel_l2:.3e}")
+
+
+def compare(gpu_out: torch.Tensor, ref64: np.ndarray, dtype: str) -> Report:
+    got = gpu_out.detach().double().cpu().numpy()
+    ref_r = oracle.round_to_dtype(ref64, dtype)
+    diff = got - ref_r
+    nr = np.linalg.norm(ref_r)
+    per_seq = [np.linalg.norm(diff[s]) / max(np.linalg.norm(ref_r[s]), 1e-30) for s in range(got.shape[0])
+               if np.linalg.norm(ref_r[s]) > 0]
+    return Report(
+        max_abs=float(np.max(np.abs(diff))) if diff.size else 0.0,
+        rel_l2=float(np.linalg.norm(diff) / nr) if nr > 0 else float(np.linalg.norm(diff)),
+        max_abs_unrounded=float(np.max(np.abs(got - ref64))) if diff.size else 0.0,
+        rel_l2_unrounded=float(np.linalg.norm(got - ref64) / max(np.linalg.norm(ref64), 1e-30)),
+        worst_seq_rel_l2=float(max(per_seq)) if per_seq else 0.0)
+
+
+def assert_close(rep: Report, dtype: str, what: str) -> None:
+    ma, rl = TOL[dtype]
+    log(f"[parity] {what}: {rep}")
+    assert np.isfinite(rep.max_abs) and np.isfinite(rep.rel_l2), f"{what}: non-finite result"
+    assert rep.max_abs <= ma, f"{what}: max-abs {rep.max_abs:.3e} > {ma}"
+    assert rep.rel_l2 <= rl, f"{what}: rel-L2 {rep.rel_l2:.3e} > {rl}"
