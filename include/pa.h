@@ -58,7 +58,7 @@ typedef enum pa_status {
     PA_OK = 0,
     PA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, Hq % Hkv != 0,
                                  non-finite scale, partition not a multiple of block_size */
-    PA_ERR_UNSUPPORTED = 2,   /* head_dim, block_size, dtype or layout outside the supported set */
+    PA_ERR_UNSUPPORTED = 2,   /* head_dim, block_size, dtype, layout or kernel outside the supported set */
     PA_ERR_WORKSPACE = 3,     /* split-K needs a workspace and the one given is missing or too small */
     PA_ERR_HIP = 4            /* a HIP launch failed */
 } pa_status;
@@ -82,6 +82,26 @@ typedef enum pa_layout {
     PA_LAYOUT_BHTD = 0,
     PA_LAYOUT_BTHD = 1
 } pa_layout;
+
+/*
+ * Kernel choice of pa_decode_ex.  Both kernels compute the same function and
+ * meet the same accuracy bound; they differ in how the work maps onto the GPU.
+ *   PA_KERNEL_AUTO    the library picks: PA_KERNEL_MFMA when its shape
+ *                     conditions hold and at least 4 q heads share a kv head,
+ *                     else PA_KERNEL_VECTOR.
+ *   PA_KERNEL_VECTOR  scores and weighted sums on the vector ALUs; any
+ *                     supported shape.
+ *   PA_KERNEL_MFMA    the q heads that share one kv head are one small dense
+ *                     contraction per 16-token tile, done on the matrix cores;
+ *                     needs f16 or bf16, head_dim 128 or 256, and
+ *                     num_q_heads/num_kv_heads <= 16 or a multiple of 16
+ *                     (PA_ERR_UNSUPPORTED otherwise).
+ */
+typedef enum pa_kernel {
+    PA_KERNEL_AUTO = 0,
+    PA_KERNEL_VECTOR = 1,
+    PA_KERNEL_MFMA = 2
+} pa_kernel;
 
 /* Supported shapes: head_dim in {32, 64, 128, 256}; block_size in {8, 16, 32};
  * any num_q_heads that is a multiple of num_kv_heads. */
@@ -111,7 +131,7 @@ typedef enum pa_layout {
  *                  its content on entry does not matter
  *
  * Equivalent to pa_decode_ex with num_blocks = INT32_MAX (table entries are
- * trusted), layout PA_LAYOUT_BHTD and partition_tokens = 0.
+ * trusted), layout PA_LAYOUT_BHTD, partition_tokens = 0 and PA_KERNEL_AUTO.
  */
 pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, const int32_t *context_lens,
@@ -120,8 +140,8 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * pa_decode_ex -- pa_decode with the pool size, the cache layout and the
- * split-K partition made explicit.
+ * pa_decode_ex -- pa_decode with the pool size, the cache layout, the
+ * split-K partition and the kernel made explicit.
  *
  *   num_blocks        blocks in the pool; a table entry outside [0, num_blocks)
  *                     contributes no tokens instead of being read
@@ -131,6 +151,7 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
  *                     N > 0 = each workgroup reads at most N tokens of one
  *                     sequence (N a multiple of block_size) and a reduce kernel
  *                     merges the partitions' (max, sum, partial output).
+ *   kernel            PA_KERNEL_AUTO, PA_KERNEL_VECTOR or PA_KERNEL_MFMA (above)
  *
  * Per-block partial results are combined with a running max and sum
  * ("online softmax"); the combine across partitions is the same operation.
@@ -139,7 +160,7 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
                        const int32_t *block_tables, const int32_t *context_lens,
                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                        int block_size, int max_blocks_per_seq, int num_blocks, float scale,
-                       pa_dtype dtype, pa_layout layout, int partition_tokens,
+                       pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*

@@ -22,8 +22,21 @@ bool supported_head_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 2
 bool supported_block_size(int b) { return b == 8 || b == 16 || b == 32; }
 bool supported_dtype(pa_dtype t) { return t == PA_F32 || t == PA_F16 || t == PA_BF16; }
 bool supported_layout(pa_layout l) { return l == PA_LAYOUT_BHTD || l == PA_LAYOUT_BTHD; }
+bool supported_kernel(pa_kernel k) { return k == PA_KERNEL_AUTO || k == PA_KERNEL_VECTOR || k == PA_KERNEL_MFMA; }
+
+// The matrix-core kernel needs 16-bit elements, head_dim a multiple of 128
+// and q-head groups that fill at most 16 columns per workgroup.
+bool mfma_shape(pa_dtype dtype, int head_dim, int group)
+{
+    return dtype != PA_F32 && (head_dim == 128 || head_dim == 256) && (group <= 16 || group % 16 == 0);
+}
+
+// Smallest q-head group the library sends to the matrix cores on its own:
+// below it the per-token vector work is small enough for the VALU.
+constexpr int MFMA_MIN_GROUP = 4;
 
 struct Plan {
+    bool mfma = false;          // grouped-query matrix-core kernel
     int partition_blocks = 0;   // blocks per partition
     int max_partitions = 1;     // grid x extent
     int gt = 1;                 // q heads per workgroup
@@ -58,12 +71,19 @@ pa_status check_sizes(int num_seqs, int num_q_heads, int num_kv_heads, int head_
 }
 
 pa_status make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                    int max_blocks_per_seq, pa_dtype dtype, int partition_tokens, Plan *pl)
+                    int max_blocks_per_seq, pa_dtype dtype, int partition_tokens, pa_kernel kernel, Plan *pl)
 {
     pa_status st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                max_blocks_per_seq, dtype, partition_tokens);
     if (st != PA_OK)
         return st;
+    if (!supported_kernel(kernel))
+        return PA_ERR_UNSUPPORTED;
+    const int group = num_q_heads / num_kv_heads;
+    const bool mfma_ok = mfma_shape(dtype, head_dim, group);
+    if (kernel == PA_KERNEL_MFMA && !mfma_ok)
+        return PA_ERR_UNSUPPORTED;
+    pl->mfma = kernel == PA_KERNEL_MFMA || (kernel == PA_KERNEL_AUTO && mfma_ok && group >= MFMA_MIN_GROUP);
     int pt = partition_tokens == 0 ? auto_partition_tokens(block_size, max_blocks_per_seq) : partition_tokens;
     const long long max_tokens = (long long)block_size * max_blocks_per_seq;
     if (pt < 0 || pt >= max_tokens) {
@@ -73,8 +93,10 @@ pa_status make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_di
         pl->partition_blocks = pt / block_size;
         pl->max_partitions = (max_blocks_per_seq + pl->partition_blocks - 1) / pl->partition_blocks;
     }
-    const int group = num_q_heads / num_kv_heads;
-    pl->gt = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    if (pl->mfma)
+        pl->gt = group <= 16 ? group : 16;
+    else
+        pl->gt = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
     pl->group_split = group / pl->gt;
     if ((long long)num_kv_heads * pl->group_split > 65535 || num_seqs > 65535)
         return PA_ERR_UNSUPPORTED;
@@ -116,7 +138,7 @@ pa_status pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_he
         return PA_ERR_INVALID_ARG;
     Plan pl;
     pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                             max_blocks_per_seq, dtype, partition_tokens, &pl);
+                             max_blocks_per_seq, dtype, partition_tokens, PA_KERNEL_AUTO, &pl);
     *bytes_out = st == PA_OK ? pl.ws_bytes : 0;
     return st;
 }
@@ -125,12 +147,12 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
                        const int32_t *block_tables, const int32_t *context_lens,
                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                        int block_size, int max_blocks_per_seq, int num_blocks, float scale,
-                       pa_dtype dtype, pa_layout layout, int partition_tokens,
+                       pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
                        void *workspace, size_t workspace_bytes, void *stream)
 {
     Plan pl;
     pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                             max_blocks_per_seq, dtype, partition_tokens, &pl);
+                             max_blocks_per_seq, dtype, partition_tokens, kernel, &pl);
     if (st != PA_OK)
         return st;
     if (!supported_layout(layout))
@@ -173,10 +195,15 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    switch (dtype) {
-    case PA_F32: e = pa::launch_decode_f32(p, head_dim, block_size, pl.gt, s); break;
-    case PA_F16: e = pa::launch_decode_f16(p, head_dim, block_size, pl.gt, s); break;
-    default: e = pa::launch_decode_bf16(p, head_dim, block_size, pl.gt, s); break;
+    if (pl.mfma) {
+        e = dtype == PA_F16 ? pa::launch_mfma_f16(p, head_dim, block_size, s)
+                            : pa::launch_mfma_bf16(p, head_dim, block_size, s);
+    } else {
+        switch (dtype) {
+        case PA_F32: e = pa::launch_decode_f32(p, head_dim, block_size, pl.gt, s); break;
+        case PA_F16: e = pa::launch_decode_f16(p, head_dim, block_size, pl.gt, s); break;
+        default: e = pa::launch_decode_bf16(p, head_dim, block_size, pl.gt, s); break;
+        }
     }
     if (e != hipSuccess)
         return PA_ERR_HIP;
@@ -196,7 +223,7 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
 {
     return pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, INT32_MAX, scale, dtype,
-                        PA_LAYOUT_BHTD, 0, workspace, workspace_bytes, stream);
+                        PA_LAYOUT_BHTD, 0, PA_KERNEL_AUTO, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_cache,

@@ -1,0 +1,13 @@
+// pa_decode_mfma_f16.hip -- instantiates the grouped-query (matrix core) decode
+// kernels for f16 storage.
+#include "pa_decode_mfma.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+hipError_t launch_mfma_f16(const DecodeParams &p, int head_dim, int block_size, hipStream_t st)
+{
+    return launch_mfma_dtype<f16_t>(p, head_dim, block_size, st);
+}
+
+}  // namespace pa

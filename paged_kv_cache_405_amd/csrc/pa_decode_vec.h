@@ -32,130 +32,102 @@
 
 namespace pa {
 
-template <typename T, int D, int BS, int GT, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams P)
-{
+// One wave's share of the work on one (sequence, kv head): the online-softmax
+// state of GT query heads and the step pipeline that feeds it.  A step is a
+// slab of NLD wave-wide loads of K and of V inside one (block, kv head) tile.
+// The pipeline is the one of the grouped-query kernel: two register buffers
+// alternate, the next step's loads are issued unconditionally before the
+// current step's math, and block-table entries are wave-uniform scalar loads
+// fetched one step further ahead.
+template <typename T, int D, int BS, int GT>
+struct VecWorker {
     using V = Vec<T>;
-    constexpr int VEC = V::N;                 // elements per 16 bytes
-    constexpr int ES = 16 / VEC;              // element bytes
-    constexpr int LPT = D / VEC;              // lanes per token row
+    static constexpr int VEC = V::N;                 // elements per 16 bytes
+    static constexpr int ES = 16 / VEC;              // element bytes
+    static constexpr int LPT = D / VEC;              // lanes per token row
     static_assert(LPT >= 1 && LPT <= 64 && (64 % LPT) == 0, "head_dim / dtype combination");
-    constexpr int TPL = 64 / LPT;             // token rows per wave-wide load
-    constexpr int ROWS = TPL < BS ? TPL : BS; // rows that carry tokens
-    constexpr bool ALL_ROWS = TPL <= BS;
-    constexpr int NLD_TILE = BS / ROWS;       // wave-wide loads per (block, kv head) tile
-    constexpr int NLD = NLD_TILE < 4 ? NLD_TILE : 4;   // loads per step (a slab of the tile)
-    constexpr int NSLAB = NLD_TILE / NLD;     // steps per tile
-    constexpr int SLAB_TOK = NLD * ROWS;      // tokens per step
+    static constexpr int TPL = 64 / LPT;             // token rows per wave-wide load
+    static constexpr int ROWS = TPL < BS ? TPL : BS; // rows that carry tokens
+    static constexpr bool ALL_ROWS = TPL <= BS;
+    static constexpr int NLD_TILE = BS / ROWS;       // wave-wide loads per (block, kv head) tile
+    static constexpr int NLD = NLD_TILE < 4 ? NLD_TILE : 4;   // loads per step (a slab of the tile)
+    static constexpr int NSLAB = NLD_TILE / NLD;     // steps per tile
+    static constexpr int SLAB_TOK = NLD * ROWS;      // tokens per step
 
-    const int p = blockIdx.x;
-    const int hg = blockIdx.y;
-    const int s = blockIdx.z;
-
-    int ctx = P.ctx[s];
-    const int cap = P.max_blocks * BS;
-    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-    const int nblk = (ctx + BS - 1) / BS;
-    const int npart = nblk == 0 ? 1 : (nblk + P.partition_blocks - 1) / P.partition_blocks;
-    if (p >= npart)
-        return;
-
-    const int kvh = hg / P.group_split;
-    const int qh0 = kvh * P.group + (hg - kvh * P.group_split) * GT;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int row = lane / LPT;
-    const int chunk = lane % LPT;
-    const bool row_on = ALL_ROWS || row < ROWS;
-    const int row_c = row_on ? row : 0;
-
-    float qf[GT][VEC];
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-        const int64_t qi = ((int64_t)s * P.num_q_heads + qh0 + g) * D + chunk * VEC;
-        V::widen(ld16(static_cast<const char *>(P.q) + qi * ES), qf[g]);
-    }
-
-    float m[GT], l[GT], acc[GT][VEC];
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-        m[g] = NEG_BIG;
-        l[g] = 0.f;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            acc[g][e] = 0.f;
-    }
-
-    const int64_t lane_off = ((int64_t)kvh * P.head_stride + (int64_t)row_c * P.token_stride + chunk * VEC) * ES;
-    const char *kb = static_cast<const char *>(P.k) + lane_off;
-    const char *vb = static_cast<const char *>(P.v) + lane_off;
-    const int64_t blk_bytes = P.block_stride * ES;
-    const int64_t ld_bytes = (int64_t)ROWS * P.token_stride * ES;
-    const int32_t *trow = P.tables + (int64_t)s * P.max_blocks;
-
-    const int b0 = p * P.partition_blocks;
-    const int b1 = min(nblk, b0 + P.partition_blocks);
-    const int q1 = (b1 - b0) * NSLAB;         // steps in this partition
-
-    // one step = NLD wave-wide loads of K and of V (a slab of one tile)
-    auto load_step = [&](int q, uint4 *kd, uint4 *vd) {
-        const int j = b0 + q / NSLAB;
-        const int sl = q % NSLAB;
-        const int phys = trow[j];
-        const bool ok = (unsigned)phys < (unsigned)P.num_blocks;
-        const int64_t boff = (int64_t)(ok ? phys : 0) * blk_bytes + (int64_t)sl * NLD * ld_bytes;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            kd[i] = ld16(kb + boff + i * ld_bytes);
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            vd[i] = ld16(vb + boff + i * ld_bytes);
-        return ok;
+    struct Buf {
+        uint4 k[NLD];
+        uint4 v[NLD];
+        bool ok;
     };
 
-    uint4 kr[NLD], vr[NLD], kn[NLD], vn[NLD];
+    const char *kb;           // K of this kv head at this lane's (row, chunk)
+    const char *vb;
+    const int32_t *trow;
+    int64_t blk_bytes, ld_bytes;
+    int num_blocks;
+    int ctx;
+    float scale_log2;
+    int row;
+    bool row_on;
+    float qf[GT][VEC];
+
+    float m[GT], l[GT], acc[GT][VEC];   // per token row; rows are merged at the end
+
+    __device__ __forceinline__ void reset() {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i)
-        kn[i] = vn[i] = make_uint4(0u, 0u, 0u, 0u);
-    int q = wave;
-    bool ok_cur = false;
-    if (q < q1)
-        ok_cur = load_step(q, kr, vr);
+        for (int g = 0; g < GT; ++g) {
+            m[g] = NEG_BIG;
+            l[g] = 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                acc[g][e] = 0.f;
+        }
+    }
 
-    for (; q < q1; q += NW) {
-        bool ok_next = false;
-        if (q + NW < q1)
-            ok_next = load_step(q + NW, kn, vn);
-        const int t0 = (b0 + q / NSLAB) * BS + (q % NSLAB) * SLAB_TOK;   // first token of the step
+    // step q of the sequence: block q / NSLAB (a scalar load), slab q % NSLAB
+    __device__ __forceinline__ int phys(int q) const { return trow[q / NSLAB]; }
 
+    __device__ __forceinline__ void load(int q, int ph, Buf &b) const {
+        b.ok = (unsigned)ph < (unsigned)num_blocks;
+        const int64_t boff = (int64_t)(b.ok ? ph : 0) * blk_bytes + (int64_t)(q % NSLAB) * NLD * ld_bytes;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            b.k[i] = ld16(kb + boff + i * ld_bytes);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            b.v[i] = ld16(vb + boff + i * ld_bytes);
+    }
+
+    __device__ __forceinline__ void compute(int q, const Buf &b) {
+        const int t0 = q * SLAB_TOK;             // first token of the step
         // scores of this step, log2 units
         float sc[GT][NLD];
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             float kf[VEC];
-            V::widen(kr[i], kf);
+            V::widen(b.k[i], kf);
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
                 float d = 0.f;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     d = fmaf(qf[g][e], kf[e], d);
-                sc[g][i] = group_sum<LPT>(d) * P.scale_log2;
+                sc[g][i] = group_sum<LPT>(d) * scale_log2;
             }
         }
         float vf[NLD][VEC];
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
-            V::widen(vr[i], vf[i]);
+            V::widen(b.v[i], vf[i]);
 
         // tokens past the context, of an unmapped block, or of an idle row:
         // select (never multiply) so that whatever the memory holds is ignored
-        const bool full = ok_cur && t0 + SLAB_TOK <= ctx && ALL_ROWS;
+        const bool full = b.ok && t0 + SLAB_TOK <= ctx && ALL_ROWS;
         if (!full) {
 #pragma unroll
             for (int i = 0; i < NLD; ++i) {
                 const int t = t0 + i * ROWS + row;
-                const bool valid = ok_cur && row_on && t < ctx;
+                const bool valid = b.ok && row_on && t < ctx;
                 if (!valid) {
 #pragma unroll
                     for (int g = 0; g < GT; ++g)
@@ -193,32 +165,108 @@ __global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams 
             }
             m[g] = mn;
         }
+    }
 
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            kr[i] = kn[i];
-            vr[i] = vn[i];
+    // steps qbeg, qbeg + stride, ... below qend (wave-uniform); same loop
+    // shape as the grouped-query kernel: pairs of steps, one back edge,
+    // unconditional next-step loads
+    __device__ __forceinline__ void run(int qbeg, int qend, int stride) {
+        if (qbeg >= qend)
+            return;
+        const int n = (qend - 1 - qbeg) / stride + 1;
+        const int qlast = qbeg + (n - 1) * stride;
+        Buf b0, b1;
+        int q = qbeg;
+        load(q, phys(q), b0);
+        int pn = phys(min(q + stride, qlast));
+        for (int it = 1; it < n; it += 2) {
+            load(min(q + stride, qlast), pn, b1);
+            pn = phys(min(q + 2 * stride, qlast));
+            __builtin_amdgcn_sched_barrier(0);   // next loads go out before this step's math
+            compute(q, b0);
+            load(min(q + 2 * stride, qlast), pn, b0);
+            pn = phys(min(q + 3 * stride, qlast));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(q + stride, b1);
+            q += 2 * stride;
         }
-        ok_cur = ok_next;
+        if (n & 1)
+            compute(q, b0);
     }
 
     // merge the token rows of the wave (lanes that differ in the row bits)
+    __device__ __forceinline__ void merge_rows() {
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
+        for (int off = LPT; off < 64; off <<= 1) {
 #pragma unroll
-        for (int g = 0; g < GT; ++g) {
-            const float mo = __shfl_xor(m[g], off);
-            const float lo = __shfl_xor(l[g], off);
-            const float mn = fmaxf(m[g], mo);
-            const float a = fast_exp2(m[g] - mn);
-            const float b = fast_exp2(mo - mn);
-            l[g] = l[g] * a + lo * b;
+            for (int g = 0; g < GT; ++g) {
+                const float mo = __shfl_xor(m[g], off);
+                const float lo = __shfl_xor(l[g], off);
+                const float mn = fmaxf(m[g], mo);
+                const float a = fast_exp2(m[g] - mn);
+                const float c = fast_exp2(mo - mn);
+                l[g] = l[g] * a + lo * c;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                acc[g][e] = acc[g][e] * a + __shfl_xor(acc[g][e], off) * b;
-            m[g] = mn;
+                for (int e = 0; e < VEC; ++e)
+                    acc[g][e] = acc[g][e] * a + __shfl_xor(acc[g][e], off) * c;
+                m[g] = mn;
+            }
         }
     }
+};
+
+template <typename T, int D, int BS, int GT, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams P)
+{
+    using W = VecWorker<T, D, BS, GT>;
+    constexpr int VEC = W::VEC;
+    constexpr int ES = W::ES;
+    constexpr int LPT = W::LPT;
+
+    const int p = blockIdx.x;
+    const int hg = blockIdx.y;
+    const int s = blockIdx.z;
+
+    int ctx = P.ctx[s];
+    const int cap = P.max_blocks * BS;
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    const int nblk = (ctx + BS - 1) / BS;
+    const int npart = nblk == 0 ? 1 : (nblk + P.partition_blocks - 1) / P.partition_blocks;
+    if (p >= npart)
+        return;
+
+    const int kvh = hg / P.group_split;
+    const int qh0 = kvh * P.group + (hg - kvh * P.group_split) * GT;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row = lane / LPT;
+    const int chunk = lane % LPT;
+
+    W w;
+    w.row = row;
+    w.row_on = W::ALL_ROWS || row < W::ROWS;
+    const int row_c = w.row_on ? row : 0;
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        const int64_t qi = ((int64_t)s * P.num_q_heads + qh0 + g) * D + chunk * VEC;
+        W::V::widen(ld16(static_cast<const char *>(P.q) + qi * ES), w.qf[g]);
+    }
+    const int64_t lane_off = ((int64_t)kvh * P.head_stride + (int64_t)row_c * P.token_stride + chunk * VEC) * ES;
+    w.kb = static_cast<const char *>(P.k) + lane_off;
+    w.vb = static_cast<const char *>(P.v) + lane_off;
+    w.blk_bytes = P.block_stride * ES;
+    w.ld_bytes = (int64_t)W::ROWS * P.token_stride * ES;
+    w.trow = P.tables + (int64_t)s * P.max_blocks;
+    w.num_blocks = P.num_blocks;
+    w.ctx = ctx;
+    w.scale_log2 = P.scale_log2;
+    w.reset();
+
+    // the partition's steps, taken round robin by the waves
+    const int b0 = p * P.partition_blocks;
+    const int b1 = min(nblk, b0 + P.partition_blocks);
+    w.run(b0 * W::NSLAB + wave, b1 * W::NSLAB, NW);
+    w.merge_rows();
 
     const bool single = npart == 1;
     auto emit = [&](int g, int d, float M, float L, float A) {
@@ -239,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams 
             for (int g = 0; g < GT; ++g)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                    emit(g, chunk * VEC + e, m[g], l[g], acc[g][e]);
+                    emit(g, chunk * VEC + e, w.m[g], w.l[g], w.acc[g][e]);
         }
     } else {
         __shared__ float sm_m[NW][GT], sm_l[NW][GT];
@@ -249,13 +297,13 @@ __global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams 
             for (int g = 0; g < GT; ++g)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                    sm_acc[wave][g][chunk * VEC + e] = acc[g][e];
+                    sm_acc[wave][g][chunk * VEC + e] = w.acc[g][e];
         }
         if (lane == 0) {
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
-                sm_m[wave][g] = m[g];
-                sm_l[wave][g] = l[g];
+                sm_m[wave][g] = w.m[g];
+                sm_l[wave][g] = w.l[g];
             }
         }
         __syncthreads();
@@ -264,14 +312,14 @@ __global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams 
             const int d = idx - g * D;
             float M = sm_m[0][g];
 #pragma unroll
-            for (int w = 1; w < NW; ++w)
-                M = fmaxf(M, sm_m[w][g]);
+            for (int v = 1; v < NW; ++v)
+                M = fmaxf(M, sm_m[v][g]);
             float L = 0.f, A = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float c = fast_exp2(sm_m[w][g] - M);
-                L = fmaf(sm_l[w][g], c, L);
-                A = fmaf(sm_acc[w][g][d], c, A);
+            for (int v = 0; v < NW; ++v) {
+                const float c = fast_exp2(sm_m[v][g] - M);
+                L = fmaf(sm_l[v][g], c, L);
+                A = fmaf(sm_acc[v][g][d], c, A);
             }
             emit(g, d, M, L, A);
         }

@@ -16,6 +16,10 @@ enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 hipError_t launch_decode_f32(const DecodeParams &p, int head_dim, int block_size, int gt, hipStream_t st);
 hipError_t launch_decode_f16(const DecodeParams &p, int head_dim, int block_size, int gt, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeParams &p, int head_dim, int block_size, int gt, hipStream_t st);
+// Grouped-query decode on the matrix cores: f16 / bf16, head_dim 128 or 256,
+// at most 16 q heads per workgroup (group / group_split).
+hipError_t launch_mfma_f16(const DecodeParams &p, int head_dim, int block_size, hipStream_t st);
+hipError_t launch_mfma_bf16(const DecodeParams &p, int head_dim, int block_size, hipStream_t st);
 hipError_t launch_reduce(const DecodeParams &p, int dtype, int head_dim, int block_size, hipStream_t st);
 hipError_t launch_append(const AppendParams &p, hipStream_t st);
 

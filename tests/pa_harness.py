@@ -21,6 +21,28 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat1
 # max-abs and relative-L2 bounds, against the oracle rounded to the output type
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-3), "bf16": (2e-3, 1e-3)}
 
+# fraction bits of each output type (unit in the last place of a normal x is
+# 2^(floor(log2|x|) - bits)) and its smallest subnormal step
+FRACTION_BITS = {"f32": 23, "f16": 10, "bf16": 7}
+MIN_STEP = {"f32": 2.0 ** -149, "f16": 2.0 ** -24, "bf16": 2.0 ** -133}
+
+
+def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the output type's grid at each |x| (x already representable)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(a)                                # |x| = m 2^e, 0.5 <= m < 1
+    step = np.maximum(np.ldexp(1.0, e - 1 - FRACTION_BITS[dtype]), MIN_STEP[dtype])
+    return np.where(a == 0, MIN_STEP[dtype], step)
+
+
+def elementwise_bound(ref_rounded: np.ndarray, dtype: str) -> np.ndarray:
+    """Per-element bound: the max-abs tolerance, or one unit in the last place of
+    the output type where that is coarser.  A kernel that computes in fp32 and
+    rounds once to a 16-bit type can land on either neighbour of the exact
+    value; where the type's spacing exceeds the max-abs tolerance (|out| >= 0.5
+    in bf16, >= 4 in f16) the bound is therefore that spacing."""
+    return np.maximum(TOL[dtype][0], ulp(ref_rounded, dtype))
+
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
@@ -66,13 +88,14 @@ def upload(w: Workload, layout=B.PA_LAYOUT_BHTD) -> GpuInputs:
         layout=layout)
 
 
-def gpu_step(w: Workload, g: GpuInputs, partition_tokens=0, append=True, num_blocks=None) -> torch.Tensor:
+def gpu_step(w: Workload, g: GpuInputs, partition_tokens=0, append=True, num_blocks=None,
+             kernel=B.PA_KERNEL_AUTO) -> torch.Tensor:
     """Append (if the workload has new tokens) then decode, on the current stream."""
     if append and g.slots is not None:
         B.pa_reshape_and_cache(g.new_k, g.new_v, g.k_cache, g.v_cache, g.slots, layout=g.layout)
     out = torch.empty_like(g.q)
     B.pa_decode_ex(out, g.q, g.k_cache, g.v_cache, g.tables, g.ctx, w.scale, layout=g.layout,
-                   partition_tokens=partition_tokens, num_blocks=num_blocks)
+                   partition_tokens=partition_tokens, num_blocks=num_blocks, kernel=kernel)
     return out
 
 
@@ -93,10 +116,13 @@ class Report:
     max_abs_unrounded: float
     rel_l2_unrounded: float
     worst_seq_rel_l2: float
+    over_bound: int          # elements outside max(max-abs tolerance, 1 ulp of the output type)
+    worst_ratio: float       # max |diff| / per-element bound
 
     def __str__(self):
         return (f"max_abs {self.max_abs:.3e} rel_l2 {self.rel_l2:.3e} (vs unrounded: {self.max_abs_unrounded:.3e} / "
-                f"{self.rel_l2_unrounded:.3e}); worst per-seq rel_l2 {self.worst_seq_rel_l2:.3e}")
+                f"{self.rel_l2_unrounded:.3e}); worst per-seq rel_l2 {self.worst_seq_rel_l2:.3e}; "
+                f"worst |diff|/bound {self.worst_ratio:.3f}, {self.over_bound} over")
 
 
 def compare(gpu_out: torch.Tensor, ref64: np.ndarray, dtype: str) -> Report:
@@ -106,17 +132,22 @@ def compare(gpu_out: torch.Tensor, ref64: np.ndarray, dtype: str) -> Report:
     nr = np.linalg.norm(ref_r)
     per_seq = [np.linalg.norm(diff[s]) / max(np.linalg.norm(ref_r[s]), 1e-30) for s in range(got.shape[0])
                if np.linalg.norm(ref_r[s]) > 0]
+    bound = elementwise_bound(ref_r, dtype)
+    ratio = np.abs(diff) / bound
     return Report(
         max_abs=float(np.max(np.abs(diff))) if diff.size else 0.0,
         rel_l2=float(np.linalg.norm(diff) / nr) if nr > 0 else float(np.linalg.norm(diff)),
         max_abs_unrounded=float(np.max(np.abs(got - ref64))) if diff.size else 0.0,
         rel_l2_unrounded=float(np.linalg.norm(got - ref64) / max(np.linalg.norm(ref64), 1e-30)),
-        worst_seq_rel_l2=float(max(per_seq)) if per_seq else 0.0)
+        worst_seq_rel_l2=float(max(per_seq)) if per_seq else 0.0,
+        over_bound=int(np.count_nonzero(~(ratio <= 1.0))),
+        worst_ratio=float(np.max(ratio)) if ratio.size else 0.0)
 
 
 def assert_close(rep: Report, dtype: str, what: str) -> None:
     ma, rl = TOL[dtype]
     log(f"[parity] {what}: {rep}")
     assert np.isfinite(rep.max_abs) and np.isfinite(rep.rel_l2), f"{what}: non-finite result"
-    assert rep.max_abs <= ma, f"{what}: max-abs {rep.max_abs:.3e} > {ma}"
+    assert rep.over_bound == 0, (f"{what}: {rep.over_bound} elements beyond max({ma}, 1 ulp); "
+                                 f"max-abs {rep.max_abs:.3e}, worst |diff|/bound {rep.worst_ratio:.3f}")
     assert rep.rel_l2 <= rl, f"{what}: rel-L2 {rep.rel_l2:.3e} > {rl}"

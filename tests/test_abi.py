@@ -94,11 +94,11 @@ FAKE = 0x7f0000000000   # 16-byte aligned, never dereferenced
 
 def _decode(**kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, S=2, Hq=4, Hkv=2, D=64, bs=16, MB=8, NB=32,
-             scale=0.125, dt=B.PA_F16, layout=B.PA_LAYOUT_BHTD, pt=-1, ws=None, wsb=0)
+             scale=0.125, dt=B.PA_F16, layout=B.PA_LAYOUT_BHTD, pt=-1, kern=B.PA_KERNEL_AUTO, ws=None, wsb=0)
     a.update(kw)
     return B.lib().pa_decode_ex(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["Hq"], a["Hkv"],
                                 a["D"], a["bs"], a["MB"], a["NB"], a["scale"], a["dt"], a["layout"], a["pt"],
-                                a["ws"], a["wsb"], None)
+                                a["kern"], a["ws"], a["wsb"], None)
 
 
 def test_empty_batch_is_a_noop():
@@ -127,6 +127,10 @@ def test_empty_batch_is_a_noop():
     (dict(D=96), B.PA_ERR_UNSUPPORTED),
     (dict(layout=2), B.PA_ERR_UNSUPPORTED),
     (dict(dt=9), B.PA_ERR_UNSUPPORTED),
+    (dict(kern=3), B.PA_ERR_UNSUPPORTED),
+    (dict(kern=B.PA_KERNEL_MFMA), B.PA_ERR_UNSUPPORTED),                  # head_dim 64
+    (dict(kern=B.PA_KERNEL_MFMA, D=128, dt=B.PA_F32), B.PA_ERR_UNSUPPORTED),
+    (dict(kern=B.PA_KERNEL_MFMA, D=128, Hq=24, Hkv=1), B.PA_ERR_UNSUPPORTED),  # group 24: not <= 16, not 16k
     (dict(pt=64, MB=64), B.PA_ERR_WORKSPACE),                       # split needs a workspace
     (dict(pt=64, MB=64, ws=FAKE, wsb=16), B.PA_ERR_WORKSPACE),      # too small
     (dict(pt=64, MB=64, ws=FAKE + 8, wsb=1 << 30), B.PA_ERR_WORKSPACE),  # misaligned
