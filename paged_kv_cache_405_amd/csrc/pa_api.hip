@@ -7,6 +7,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -37,6 +40,9 @@ constexpr int MFMA_MIN_GROUP = 4;
 
 struct Plan {
     bool mfma = false;          // grouped-query matrix-core kernel
+    bool stream = false;        // balanced schedule (partition_tokens == 0)
+    int n_waves = 0;            // stream: logical waves (one workgroup each)
+    size_t off_next = 0, off_ml = 0, off_acc = 0;   // stream: workspace sections
     int partition_blocks = 0;   // blocks per partition
     int max_partitions = 1;     // grid x extent
     int gt = 1;                 // q heads per workgroup
@@ -44,15 +50,6 @@ struct Plan {
     size_t ml_bytes = 0;        // (max, sum) pairs, first in the workspace
     size_t ws_bytes = 0;        // total workspace (0 = single pass)
 };
-
-// Partition length the library picks when the caller passes 0: contexts that
-// can exceed 512 tokens are cut into 512-token partitions so that long and
-// ragged batches spread over many workgroups.
-int auto_partition_tokens(int block_size, int max_blocks)
-{
-    const long long max_tokens = (long long)block_size * max_blocks;
-    return max_tokens > 512 ? 512 : -1;
-}
 
 pa_status check_sizes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                       int max_blocks_per_seq, pa_dtype dtype, int partition_tokens)
@@ -70,6 +67,43 @@ pa_status check_sizes(int num_seqs, int num_q_heads, int num_kv_heads, int head_
     return PA_OK;
 }
 
+// Workgroups of the stream kernel for this shape that one compute unit of the
+// current device holds at once, cached per (device, kernel shape).  Returns 0
+// when there is no device or the query fails.
+int stream_occupancy(pa_dtype dtype, bool mfma, int head_dim, int block_size, int gt, int *cus)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || *cus <= 0)
+        return 0;
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int, int, int, int>, int> cache;
+    const auto key = std::make_tuple(dev, (int)dtype, (int)mfma, head_dim, block_size, gt);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = cache.find(key);
+        if (it != cache.end())
+            return it->second;
+    }
+    int occ = 0;
+    hipError_t e;
+    if (mfma)
+        e = dtype == PA_F16 ? pa::stream_mfma_f16(nullptr, head_dim, block_size, nullptr, &occ)
+                            : pa::stream_mfma_bf16(nullptr, head_dim, block_size, nullptr, &occ);
+    else if (dtype == PA_F32)
+        e = pa::stream_vec_f32(nullptr, head_dim, block_size, gt, nullptr, &occ);
+    else if (dtype == PA_F16)
+        e = pa::stream_vec_f16(nullptr, head_dim, block_size, gt, nullptr, &occ);
+    else
+        e = pa::stream_vec_bf16(nullptr, head_dim, block_size, gt, nullptr, &occ);
+    if (e != hipSuccess || occ <= 0)
+        return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = occ;
+    return occ;
+}
+
 pa_status make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                     int max_blocks_per_seq, pa_dtype dtype, int partition_tokens, pa_kernel kernel, Plan *pl)
 {
@@ -84,9 +118,9 @@ pa_status make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_di
     if (kernel == PA_KERNEL_MFMA && !mfma_ok)
         return PA_ERR_UNSUPPORTED;
     pl->mfma = kernel == PA_KERNEL_MFMA || (kernel == PA_KERNEL_AUTO && mfma_ok && group >= MFMA_MIN_GROUP);
-    int pt = partition_tokens == 0 ? auto_partition_tokens(block_size, max_blocks_per_seq) : partition_tokens;
+    const int pt = partition_tokens;
     const long long max_tokens = (long long)block_size * max_blocks_per_seq;
-    if (pt < 0 || pt >= max_tokens) {
+    if (pt <= 0 || pt >= max_tokens) {      // balanced schedule (0) or single pass
         pl->partition_blocks = max_blocks_per_seq;
         pl->max_partitions = 1;
     } else {
@@ -100,6 +134,28 @@ pa_status make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_di
     pl->group_split = group / pl->gt;
     if ((long long)num_kv_heads * pl->group_split > 65535 || num_seqs > 65535)
         return PA_ERR_UNSUPPORTED;
+    if (partition_tokens == 0) {
+        // balanced schedule: as many one-wave workgroups as the device holds at
+        // once (a multiple of 8, one share per XCD), pieces for cut units
+        int cus = 0;
+        const int occ = stream_occupancy(dtype, pl->mfma, head_dim, block_size, pl->gt, &cus);
+        if (occ <= 0)
+            return PA_ERR_HIP;
+        long long waves = (long long)cus * occ / 8 * 8;
+        waves = waves < 8 ? 8 : (waves > (1 << 20) ? (1 << 20) : waves);
+        pl->stream = true;
+        pl->n_waves = (int)waves;
+        pl->partition_blocks = max_blocks_per_seq;
+        pl->max_partitions = 1;
+        const size_t units = (size_t)num_seqs * num_kv_heads * pl->group_split;
+        const size_t pieces = 2 * (size_t)pl->n_waves;
+        pl->off_next = round_up(units * sizeof(int32_t), WS_ALIGN);
+        pl->off_ml = pl->off_next + round_up(pieces * sizeof(int32_t), WS_ALIGN);
+        pl->off_acc = pl->off_ml + round_up(pieces * pl->gt * sizeof(float2), WS_ALIGN);
+        pl->ws_bytes = pl->off_acc + pieces * pl->gt * (size_t)head_dim * sizeof(float);
+        pl->ml_bytes = 0;
+        return PA_OK;
+    }
     if (pl->max_partitions > 1) {
         const size_t units = (size_t)num_seqs * num_q_heads * pl->max_partitions;
         pl->ml_bytes = round_up(units * sizeof(float2), WS_ALIGN);
@@ -136,11 +192,24 @@ pa_status pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_he
 {
     if (!bytes_out)
         return PA_ERR_INVALID_ARG;
+    // enough for whichever kernel the call picks
+    *bytes_out = 0;
     Plan pl;
     pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                             max_blocks_per_seq, dtype, partition_tokens, PA_KERNEL_AUTO, &pl);
-    *bytes_out = st == PA_OK ? pl.ws_bytes : 0;
-    return st;
+                             max_blocks_per_seq, dtype, partition_tokens, PA_KERNEL_VECTOR, &pl);
+    if (st != PA_OK)
+        return st;
+    size_t bytes = pl.ws_bytes;
+    if (mfma_shape(dtype, head_dim, num_q_heads / num_kv_heads)) {
+        Plan pm;
+        st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
+                       partition_tokens, PA_KERNEL_MFMA, &pm);
+        if (st != PA_OK)
+            return st;
+        bytes = pm.ws_bytes > bytes ? pm.ws_bytes : bytes;
+    }
+    *bytes_out = bytes;
+    return PA_OK;
 }
 
 pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -150,11 +219,15 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
                        pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
                        void *workspace, size_t workspace_bytes, void *stream)
 {
-    Plan pl;
-    pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                             max_blocks_per_seq, dtype, partition_tokens, kernel, &pl);
+    // argument checks (no HIP call), then the launch plan (which may query the
+    // device for the balanced schedule), then the workspace
+    pa_status st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                               dtype, partition_tokens);
     if (st != PA_OK)
         return st;
+    if (!supported_kernel(kernel) || (kernel == PA_KERNEL_MFMA &&
+                                      !mfma_shape(dtype, head_dim, num_q_heads / num_kv_heads)))
+        return PA_ERR_UNSUPPORTED;
     if (!supported_layout(layout))
         return PA_ERR_UNSUPPORTED;
     if (num_blocks <= 0 || !std::isfinite(scale))
@@ -166,6 +239,11 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return PA_ERR_INVALID_ARG;
+    Plan pl;
+    st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
+                   partition_tokens, kernel, &pl);
+    if (st != PA_OK)
+        return st;
     if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned(workspace, 16)))
         return PA_ERR_WORKSPACE;
 
@@ -177,7 +255,14 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
     p.v = v_cache;
     p.tables = block_tables;
     p.ctx = context_lens;
-    if (pl.ws_bytes > 0) {
+    if (pl.stream) {
+        char *ws = static_cast<char *>(workspace);
+        p.n_waves = pl.n_waves;
+        p.unit_first = reinterpret_cast<int32_t *>(ws);
+        p.piece_next = reinterpret_cast<int32_t *>(ws + pl.off_next);
+        p.piece_ml = reinterpret_cast<float2 *>(ws + pl.off_ml);
+        p.piece_acc = reinterpret_cast<float *>(ws + pl.off_acc);
+    } else if (pl.ws_bytes > 0) {
         p.ws_ml = reinterpret_cast<float2 *>(workspace);
         p.ws_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ml_bytes);
     }
@@ -195,6 +280,20 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    if (pl.stream) {
+        if (pl.mfma)
+            e = dtype == PA_F16 ? pa::stream_mfma_f16(&p, head_dim, block_size, s, nullptr)
+                                : pa::stream_mfma_bf16(&p, head_dim, block_size, s, nullptr);
+        else if (dtype == PA_F32)
+            e = pa::stream_vec_f32(&p, head_dim, block_size, pl.gt, s, nullptr);
+        else if (dtype == PA_F16)
+            e = pa::stream_vec_f16(&p, head_dim, block_size, pl.gt, s, nullptr);
+        else
+            e = pa::stream_vec_bf16(&p, head_dim, block_size, pl.gt, s, nullptr);
+        if (e != hipSuccess)
+            return PA_ERR_HIP;
+        return pa::launch_stream_reduce(p, (int)dtype, head_dim, pl.gt, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
+    }
     if (pl.mfma) {
         e = dtype == PA_F16 ? pa::launch_mfma_f16(p, head_dim, block_size, s)
                             : pa::launch_mfma_bf16(p, head_dim, block_size, s);

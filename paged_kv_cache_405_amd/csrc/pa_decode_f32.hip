@@ -10,4 +10,9 @@ hipError_t launch_decode_f32(const DecodeParams &p, int head_dim, int block_size
     return launch_decode_dtype<f32_t>(p, head_dim, block_size, gt, st);
 }
 
+hipError_t stream_vec_f32(const DecodeParams *p, int head_dim, int block_size, int gt, hipStream_t st, int *occ)
+{
+    return vec_stream_dtype<f32_t>(p, head_dim, block_size, gt, st, occ);
+}
+
 }  // namespace pa

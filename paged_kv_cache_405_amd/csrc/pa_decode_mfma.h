@@ -39,6 +39,7 @@
 #pragma once
 
 #include "pa_device.h"
+#include "pa_stream.h"
 
 namespace pa {
 
@@ -86,6 +87,10 @@ struct MfmaWorker {
         bool okv;
     };
 
+    static constexpr int STEP_TOK = MFMA_TILE;   // tokens per step of the schedule
+
+    // the unit bound to the worker: a sequence and up to 16 q heads of one kv head
+    int seq, qh0, gh;
     // addressing of one (sequence, kv head)
     const char *kbase;        // K of this kv head, plus this lane's dim offset in a K row
     const char *vbase;        // V of this kv head, plus this lane's dim offset in a V row
@@ -101,6 +106,84 @@ struct MfmaWorker {
     f32x4_t acc[NU][8];
     float m;                  // running max of head lr (log2 units), equal in the 4 lane rows
     float lp;                 // running sum over this lane's tokens
+
+    __device__ __forceinline__ void init_lane(int lane) {
+        lr = lane & 15;
+        lg = lane >> 4;
+    }
+
+    // attach the worker to head group hg of sequence s (context ctx, already
+    // clamped to the table): q of its heads, its kv head's pools, the table
+    // row.  The token window [t_lo, t_hi) is the whole context.
+    __device__ __forceinline__ void bind(const DecodeParams &P, int s, int hg, int ctx) {
+        const int kvh = hg / P.group_split;
+        seq = s;
+        gh = P.group / P.group_split;
+        qh0 = kvh * P.group + (hg - kvh * P.group_split) * gh;
+        const bool on = lr < gh;
+        const char *qp = static_cast<const char *>(P.q) +
+                         (((int64_t)s * P.num_q_heads + qh0 + (on ? lr : 0)) * D + 8 * lg) * ES;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            qb[c] = ld16(qp + 32 * c * ES);
+            if (!on)
+                qb[c] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        blk_bytes = P.block_stride * ES;
+        tok_bytes = P.token_stride * ES;
+        kbase = static_cast<const char *>(P.k) + (int64_t)kvh * P.head_stride * ES + 8 * lg * ES;
+        vbase = static_cast<const char *>(P.v) + (int64_t)kvh * P.head_stride * ES + 8 * lr * ES;
+        trow = P.tables + (int64_t)s * P.max_blocks;
+        nblk = (ctx + BS - 1) / BS;
+        num_blocks = P.num_blocks;
+        scale_log2 = P.scale_log2;
+        t_lo = 0;
+        t_hi = ctx;
+    }
+
+    // sum of head lr over all of the wave's tokens (every lane must call it)
+    __device__ __forceinline__ float total_l() const {
+        const float l = lp + __shfl_xor(lp, 16);
+        return l + __shfl_xor(l, 32);
+    }
+
+    // the unit was finished by this wave: normalise and store out[seq, qh0 + lr, :]
+    __device__ __forceinline__ void finish_out(const DecodeParams &P) const {
+        const float l = total_l();
+        if (lr >= gh)
+            return;
+        char *o = static_cast<char *>(P.out) + ((int64_t)seq * P.num_q_heads + qh0 + lr) * D * ES;
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = l > 0.f ? acc[u][e][r] / l : 0.f;
+                st16(o + 8 * (4 * lg + r + 16 * u) * ES, V::narrow(v));
+            }
+    }
+
+    // part of the unit: store the wave's (max, sum, unnormalised output) as piece `piece`
+    __device__ __forceinline__ void finish_piece(const DecodeParams &P, int piece) const {
+        const float l = total_l();
+        if (lr >= gh)
+            return;
+        float *a = P.piece_acc + ((int64_t)piece * gh + lr) * D;
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float *d = a + 8 * (4 * lg + r + 16 * u);
+                st16(d, make_uint4(__float_as_uint(acc[u][0][r]), __float_as_uint(acc[u][1][r]),
+                                   __float_as_uint(acc[u][2][r]), __float_as_uint(acc[u][3][r])));
+                st16(d + 4, make_uint4(__float_as_uint(acc[u][4][r]), __float_as_uint(acc[u][5][r]),
+                                       __float_as_uint(acc[u][6][r]), __float_as_uint(acc[u][7][r])));
+            }
+        if (lg == 0)
+            P.piece_ml[(int64_t)piece * gh + lr] = make_float2(m, l);
+    }
 
     __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -223,8 +306,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     static_assert(D % 128 == 0, "the grouped-query kernel needs head_dim 128 or 256");
     static_assert(BS % 8 == 0, "block size 8, 16 or 32");
     using W = MfmaWorker<T, D, BS>;
-    constexpr int ES = W::ES;
-    constexpr int NC = W::NC;
     constexpr int NU = W::NU;
 
     const int p = blockIdx.x;
@@ -239,34 +320,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     if (p >= npart)
         return;
 
-    const int kvh = hg / P.group_split;
-    const int gh = P.group / P.group_split;                 // query heads of this workgroup (<= 16)
-    const int qh0 = kvh * P.group + (hg - kvh * P.group_split) * gh;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     W w;
-    w.lr = lane & 15;
-    w.lg = lane >> 4;
-    {
-        const bool on = w.lr < gh;
-        const char *qp = static_cast<const char *>(P.q) +
-                         (((int64_t)s * P.num_q_heads + qh0 + (on ? w.lr : 0)) * D + 8 * w.lg) * ES;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            w.qb[c] = ld16(qp + 32 * c * ES);
-            if (!on)
-                w.qb[c] = make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
-    w.blk_bytes = P.block_stride * ES;
-    w.tok_bytes = P.token_stride * ES;
-    w.kbase = static_cast<const char *>(P.k) + (int64_t)kvh * P.head_stride * ES + 8 * w.lg * ES;
-    w.vbase = static_cast<const char *>(P.v) + (int64_t)kvh * P.head_stride * ES + 8 * w.lr * ES;
-    w.trow = P.tables + (int64_t)s * P.max_blocks;
-    w.nblk = nblk;
-    w.num_blocks = P.num_blocks;
-    w.scale_log2 = P.scale_log2;
+    w.init_lane(lane);
+    w.bind(P, s, hg, ctx);
+    const int gh = w.gh;
+    const int qh0 = w.qh0;
 
     // tokens [t_lo, t_hi) of this partition, covered by 16-token tiles [k0, k1);
     // the waves take the tiles round robin
@@ -281,8 +342,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
 
     // total of head lr over the wave's tokens
     const int lr = w.lr, lg = w.lg;
-    float l = w.lp + __shfl_xor(w.lp, 16);
-    l += __shfl_xor(l, 32);
+    const float l = w.total_l();
 
     // merge the waves through LDS
     __shared__ float sm_m[NW][MFMA_MAX_HEADS], sm_l[NW][MFMA_MAX_HEADS];
@@ -353,6 +413,33 @@ hipError_t launch_mfma_dtype(const DecodeParams &p, int head_dim, int bs, hipStr
     switch (head_dim) {
     case 128: return launch_mfma_bs<T, 128>(p, bs, st);
     case 256: return launch_mfma_bs<T, 256>(p, bs, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Balanced schedule: launch (occ == nullptr) or report the workgroups per
+// compute unit of the stream kernel for this shape (occ != nullptr).
+template <typename T, int D, int BS>
+hipError_t mfma_stream_shape(const DecodeParams *p, hipStream_t st, int *occ)
+{
+    using W = MfmaWorker<T, D, BS>;
+    if (occ) {
+        *occ = stream_occupancy<W, BS>();
+        return hipSuccess;
+    }
+    return launch_stream<W, BS>(*p, st);
+}
+
+template <typename T>
+hipError_t mfma_stream_dtype(const DecodeParams *p, int head_dim, int bs, hipStream_t st, int *occ)
+{
+    switch (head_dim * 64 + bs) {
+    case 128 * 64 + 8: return mfma_stream_shape<T, 128, 8>(p, st, occ);
+    case 128 * 64 + 16: return mfma_stream_shape<T, 128, 16>(p, st, occ);
+    case 128 * 64 + 32: return mfma_stream_shape<T, 128, 32>(p, st, occ);
+    case 256 * 64 + 8: return mfma_stream_shape<T, 256, 8>(p, st, occ);
+    case 256 * 64 + 16: return mfma_stream_shape<T, 256, 16>(p, st, occ);
+    case 256 * 64 + 32: return mfma_stream_shape<T, 256, 32>(p, st, occ);
     default: return hipErrorInvalidValue;
     }
 }

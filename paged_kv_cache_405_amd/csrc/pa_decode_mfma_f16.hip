@@ -10,4 +10,9 @@ hipError_t launch_mfma_f16(const DecodeParams &p, int head_dim, int block_size, 
     return launch_mfma_dtype<f16_t>(p, head_dim, block_size, st);
 }
 
+hipError_t stream_mfma_f16(const DecodeParams *p, int head_dim, int block_size, hipStream_t st, int *occ)
+{
+    return mfma_stream_dtype<f16_t>(p, head_dim, block_size, st, occ);
+}
+
 }  // namespace pa

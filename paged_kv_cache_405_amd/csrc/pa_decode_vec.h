@@ -29,6 +29,7 @@
 #pragma once
 
 #include "pa_device.h"
+#include "pa_stream.h"
 
 namespace pa {
 
@@ -54,12 +55,16 @@ struct VecWorker {
     static constexpr int NSLAB = NLD_TILE / NLD;     // steps per tile
     static constexpr int SLAB_TOK = NLD * ROWS;      // tokens per step
 
+    static constexpr int STEP_TOK = SLAB_TOK;        // tokens per step of the schedule
+
     struct Buf {
         uint4 k[NLD];
         uint4 v[NLD];
         bool ok;
     };
 
+    int seq, qh0;             // the unit bound to the worker: a sequence and GT q heads
+    int chunk;                // this lane's 16-byte chunk of a row
     const char *kb;           // K of this kv head at this lane's (row, chunk)
     const char *vb;
     const int32_t *trow;
@@ -72,6 +77,69 @@ struct VecWorker {
     float qf[GT][VEC];
 
     float m[GT], l[GT], acc[GT][VEC];   // per token row; rows are merged at the end
+
+    __device__ __forceinline__ void init_lane(int lane) {
+        row = lane / LPT;
+        chunk = lane % LPT;
+        row_on = ALL_ROWS || row < ROWS;
+    }
+
+    // attach the worker to head group hg of sequence s (context ctx, already
+    // clamped to the table): q of its GT heads, its kv head's pools, the table row
+    __device__ __forceinline__ void bind(const DecodeParams &P, int s, int hg, int ctx_) {
+        const int kvh = hg / P.group_split;
+        seq = s;
+        qh0 = kvh * P.group + (hg - kvh * P.group_split) * GT;
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            const int64_t qi = ((int64_t)s * P.num_q_heads + qh0 + g) * D + chunk * VEC;
+            V::widen(ld16(static_cast<const char *>(P.q) + qi * ES), qf[g]);
+        }
+        const int row_c = row_on ? row : 0;
+        const int64_t lane_off = ((int64_t)kvh * P.head_stride + (int64_t)row_c * P.token_stride + chunk * VEC) * ES;
+        kb = static_cast<const char *>(P.k) + lane_off;
+        vb = static_cast<const char *>(P.v) + lane_off;
+        blk_bytes = P.block_stride * ES;
+        ld_bytes = (int64_t)ROWS * P.token_stride * ES;
+        trow = P.tables + (int64_t)s * P.max_blocks;
+        num_blocks = P.num_blocks;
+        ctx = ctx_;
+        scale_log2 = P.scale_log2;
+    }
+
+    // the unit was finished by this wave: merge the rows, normalise, store
+    // out[seq, qh0 + g, :] from the lanes of row 0
+    __device__ __forceinline__ void finish_out(const DecodeParams &P) {
+        merge_rows();
+        if (row != 0)
+            return;
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            float v[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                v[e] = l[g] > 0.f ? acc[g][e] / l[g] : 0.f;
+            char *o = static_cast<char *>(P.out) + (((int64_t)seq * P.num_q_heads + qh0 + g) * D + chunk * VEC) * ES;
+            st16(o, V::narrow(v));
+        }
+    }
+
+    // part of the unit: store the wave's (max, sum, unnormalised output) as piece `piece`
+    __device__ __forceinline__ void finish_piece(const DecodeParams &P, int piece) {
+        merge_rows();
+        if (row != 0)
+            return;
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            float *a = P.piece_acc + ((int64_t)piece * GT + g) * D + chunk * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4)
+                st16(a + e, make_uint4(__float_as_uint(acc[g][e]), __float_as_uint(acc[g][e + 1]),
+                                       __float_as_uint(acc[g][e + 2]), __float_as_uint(acc[g][e + 3])));
+            if (chunk == 0)
+                P.piece_ml[(int64_t)piece * GT + g] = make_float2(m[g], l[g]);
+        }
+    }
 
     __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -220,8 +288,6 @@ __global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams 
 {
     using W = VecWorker<T, D, BS, GT>;
     constexpr int VEC = W::VEC;
-    constexpr int ES = W::ES;
-    constexpr int LPT = W::LPT;
 
     const int p = blockIdx.x;
     const int hg = blockIdx.y;
@@ -235,32 +301,16 @@ __global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams 
     if (p >= npart)
         return;
 
-    const int kvh = hg / P.group_split;
-    const int qh0 = kvh * P.group + (hg - kvh * P.group_split) * GT;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int row = lane / LPT;
-    const int chunk = lane % LPT;
 
     W w;
-    w.row = row;
-    w.row_on = W::ALL_ROWS || row < W::ROWS;
-    const int row_c = w.row_on ? row : 0;
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-        const int64_t qi = ((int64_t)s * P.num_q_heads + qh0 + g) * D + chunk * VEC;
-        W::V::widen(ld16(static_cast<const char *>(P.q) + qi * ES), w.qf[g]);
-    }
-    const int64_t lane_off = ((int64_t)kvh * P.head_stride + (int64_t)row_c * P.token_stride + chunk * VEC) * ES;
-    w.kb = static_cast<const char *>(P.k) + lane_off;
-    w.vb = static_cast<const char *>(P.v) + lane_off;
-    w.blk_bytes = P.block_stride * ES;
-    w.ld_bytes = (int64_t)W::ROWS * P.token_stride * ES;
-    w.trow = P.tables + (int64_t)s * P.max_blocks;
-    w.num_blocks = P.num_blocks;
-    w.ctx = ctx;
-    w.scale_log2 = P.scale_log2;
+    w.init_lane(lane);
+    w.bind(P, s, hg, ctx);
     w.reset();
+    const int row = w.row;
+    const int chunk = w.chunk;
+    const int qh0 = w.qh0;
 
     // the partition's steps, taken round robin by the waves
     const int b0 = p * P.partition_blocks;
@@ -407,6 +457,54 @@ hipError_t launch_decode_dtype(const DecodeParams &p, int head_dim, int bs, int 
     case 64: return launch_decode_bs<T, 64>(p, bs, gt, st);
     case 128: return launch_decode_bs<T, 128>(p, bs, gt, st);
     case 256: return launch_decode_bs<T, 256>(p, bs, gt, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Balanced schedule: launch (occ == nullptr) or report the workgroups per
+// compute unit of the stream kernel for this shape (occ != nullptr).
+template <typename T, int D, int BS, int GT>
+hipError_t vec_stream_shape(const DecodeParams *p, hipStream_t st, int *occ)
+{
+    using W = VecWorker<T, D, BS, GT>;
+    if (occ) {
+        *occ = stream_occupancy<W, BS>();
+        return hipSuccess;
+    }
+    return launch_stream<W, BS>(*p, st);
+}
+
+template <typename T, int D, int BS>
+hipError_t vec_stream_gt(const DecodeParams *p, int gt, hipStream_t st, int *occ)
+{
+    switch (gt) {
+    case 1: return vec_stream_shape<T, D, BS, 1>(p, st, occ);
+    case 2: return vec_stream_shape<T, D, BS, 2>(p, st, occ);
+    case 4: return vec_stream_shape<T, D, BS, 4>(p, st, occ);
+    case 8: return vec_stream_shape<T, D, BS, 8>(p, st, occ);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int D>
+hipError_t vec_stream_bs(const DecodeParams *p, int bs, int gt, hipStream_t st, int *occ)
+{
+    switch (bs) {
+    case 8: return vec_stream_gt<T, D, 8>(p, gt, st, occ);
+    case 16: return vec_stream_gt<T, D, 16>(p, gt, st, occ);
+    case 32: return vec_stream_gt<T, D, 32>(p, gt, st, occ);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t vec_stream_dtype(const DecodeParams *p, int head_dim, int bs, int gt, hipStream_t st, int *occ)
+{
+    switch (head_dim) {
+    case 32: return vec_stream_bs<T, 32>(p, bs, gt, st, occ);
+    case 64: return vec_stream_bs<T, 64>(p, bs, gt, st, occ);
+    case 128: return vec_stream_bs<T, 128>(p, bs, gt, st, occ);
+    case 256: return vec_stream_bs<T, 256>(p, bs, gt, st, occ);
     default: return hipErrorInvalidValue;
     }
 }

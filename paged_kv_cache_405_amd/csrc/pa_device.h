@@ -26,16 +26,25 @@ template <> struct Vec<f32_t> {
         f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
         f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
     }
-    __device__ __forceinline__ static void store(void *p, const float *f) {
-        *reinterpret_cast<float *>(p) = f[0];
-        reinterpret_cast<float *>(p)[1] = f[1];
-        reinterpret_cast<float *>(p)[2] = f[2];
-        reinterpret_cast<float *>(p)[3] = f[3];
+    __device__ __forceinline__ static uint4 narrow(const float *f) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                          __float_as_uint(f[3]));
     }
 };
 
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x);
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x);
+
 template <> struct Vec<f16_t> {
     static constexpr int N = 8;
+    // 8 fp32 values -> 8 f16 (nearest even) in 16 bytes
+    __device__ __forceinline__ static uint4 narrow(const float *f) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)f32_to_f16_bits(f[2 * i]) | ((uint32_t)f32_to_f16_bits(f[2 * i + 1]) << 16);
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    }
     __device__ __forceinline__ static void widen2(uint32_t w, float &a, float &b) {
         half2v h = __builtin_bit_cast(half2v, w);
         a = (float)h.x; b = (float)h.y;
@@ -48,6 +57,14 @@ template <> struct Vec<f16_t> {
 
 template <> struct Vec<bf16_t> {
     static constexpr int N = 8;
+    // 8 fp32 values -> 8 bf16 (nearest even) in 16 bytes
+    __device__ __forceinline__ static uint4 narrow(const float *f) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)f32_to_bf16_bits(f[2 * i]) | ((uint32_t)f32_to_bf16_bits(f[2 * i + 1]) << 16);
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    }
     __device__ __forceinline__ static void widen2(uint32_t w, float &a, float &b) {
         a = __uint_as_float(w << 16);
         b = __uint_as_float(w & 0xffff0000u);
@@ -198,6 +215,13 @@ struct DecodeParams {
     int group;                // q heads per kv head
     int group_split;          // workgroups sharing one kv head (each takes group/group_split q heads)
     float scale_log2;         // scale * log2(e)
+    // balanced (stream) schedule: waves take equal shares of the step stream of
+    // all (head group, sequence) units; a unit cut between waves leaves pieces
+    int n_waves;              // logical waves of the stream kernel (a multiple of 8)
+    int32_t *unit_first;      // [HG * S] first piece of each unit, -1 when one wave finished it
+    int32_t *piece_next;      // [2 * n_waves] next piece of the same unit, -1 after the last
+    float2 *piece_ml;         // [2 * n_waves][heads per unit] (max in log2 units, sum)
+    float *piece_acc;         // [2 * n_waves][heads per unit][D] unnormalised partial outputs
 };
 
 struct AppendParams {

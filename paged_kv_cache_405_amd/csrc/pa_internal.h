@@ -21,6 +21,16 @@ hipError_t launch_decode_bf16(const DecodeParams &p, int head_dim, int block_siz
 hipError_t launch_mfma_f16(const DecodeParams &p, int head_dim, int block_size, hipStream_t st);
 hipError_t launch_mfma_bf16(const DecodeParams &p, int head_dim, int block_size, hipStream_t st);
 hipError_t launch_reduce(const DecodeParams &p, int dtype, int head_dim, int block_size, hipStream_t st);
+// Balanced (stream) schedule.  With occ == nullptr: launch the stream kernel
+// for this shape on st.  With occ != nullptr: store the workgroups (one wave
+// each) of that kernel that one compute unit holds at once, launch nothing.
+hipError_t stream_vec_f32(const DecodeParams *p, int head_dim, int block_size, int gt, hipStream_t st, int *occ);
+hipError_t stream_vec_f16(const DecodeParams *p, int head_dim, int block_size, int gt, hipStream_t st, int *occ);
+hipError_t stream_vec_bf16(const DecodeParams *p, int head_dim, int block_size, int gt, hipStream_t st, int *occ);
+hipError_t stream_mfma_f16(const DecodeParams *p, int head_dim, int block_size, hipStream_t st, int *occ);
+hipError_t stream_mfma_bf16(const DecodeParams *p, int head_dim, int block_size, hipStream_t st, int *occ);
+// merge the pieces the stream kernel left (one workgroup per unit)
+hipError_t launch_stream_reduce(const DecodeParams &p, int dtype, int head_dim, int heads_per_unit, hipStream_t st);
 hipError_t launch_append(const AppendParams &p, hipStream_t st);
 
 }  // namespace pa

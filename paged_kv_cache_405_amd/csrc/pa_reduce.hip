@@ -1,6 +1,7 @@
 // pa_reduce.hip -- instantiates the split-K reduce kernel (one wave per
 // (q head, sequence)) for every element type, head_dim and block_size.
 #include "pa_decode_vec.h"
+#include "pa_stream.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -36,6 +37,30 @@ hipError_t launch_reduce(const DecodeParams &p, int dtype, int head_dim, int blo
     case DT_F32: return launch_reduce_t<f32_t>(p, head_dim, block_size, st);
     case DT_F16: return launch_reduce_t<f16_t>(p, head_dim, block_size, st);
     case DT_BF16: return launch_reduce_t<bf16_t>(p, head_dim, block_size, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+static hipError_t launch_stream_reduce_t(const DecodeParams &p, int head_dim, int heads_per_unit, hipStream_t st)
+{
+    dim3 grid(p.num_seqs, p.num_kv_heads * p.group_split);
+    switch (head_dim) {
+    case 32: hipLaunchKernelGGL((stream_reduce_kernel<T, 32>), grid, dim3(128), 0, st, p, heads_per_unit); break;
+    case 64: hipLaunchKernelGGL((stream_reduce_kernel<T, 64>), grid, dim3(128), 0, st, p, heads_per_unit); break;
+    case 128: hipLaunchKernelGGL((stream_reduce_kernel<T, 128>), grid, dim3(128), 0, st, p, heads_per_unit); break;
+    case 256: hipLaunchKernelGGL((stream_reduce_kernel<T, 256>), grid, dim3(128), 0, st, p, heads_per_unit); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_reduce(const DecodeParams &p, int dtype, int head_dim, int heads_per_unit, hipStream_t st)
+{
+    switch (dtype) {
+    case DT_F32: return launch_stream_reduce_t<f32_t>(p, head_dim, heads_per_unit, st);
+    case DT_F16: return launch_stream_reduce_t<f16_t>(p, head_dim, heads_per_unit, st);
+    case DT_BF16: return launch_stream_reduce_t<bf16_t>(p, head_dim, heads_per_unit, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -54,7 +54,6 @@ def _ws(S=4, Hq=8, Hkv=2, D=128, bs=16, MB=64, dt=B.PA_F16, pt=0):
 def test_workspace_size_rules():
     # single pass: no workspace
     assert _ws(MB=16, pt=-1) == (B.PA_OK, 0)
-    assert _ws(MB=32, pt=0) == (B.PA_OK, 0)          # 512 tokens fit one partition
     # explicit partitions: P = ceil(MB / (pt / bs)); (max,sum) pairs padded to 256 B, then fp32 partials
     S, Hq, D, bs, MB, pt = 4, 8, 128, 16, 64, 256
     P = math.ceil(MB / (pt // bs))
@@ -62,9 +61,17 @@ def test_workspace_size_rules():
     assert _ws(S=S, Hq=Hq, D=D, bs=bs, MB=MB, pt=pt) == (B.PA_OK, ml + S * Hq * P * D * 4)
     # partition covering the whole table degenerates to single pass
     assert _ws(MB=64, pt=1024) == (B.PA_OK, 0)
-    # auto splits long tables
-    st, n = _ws(MB=512, pt=0)
-    assert st == B.PA_OK and n > 0
+
+
+@host_only
+def test_balanced_schedule_needs_a_device():
+    # partition_tokens = 0 sizes the balanced schedule for the current device:
+    # with none visible the query reports a HIP failure instead of guessing
+    assert _ws(MB=512, pt=0) == (B.PA_ERR_HIP, 0)
+    assert _decode(pt=0) == B.PA_ERR_HIP
+    # argument errors still come first, before any device query
+    assert _decode(pt=0, q=None) == B.PA_ERR_INVALID_ARG
+    assert _decode(pt=0, D=96) == B.PA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw,status", [
