@@ -44,9 +44,28 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="0 = library's choice, -1 = single pass, N = split-K partition (default: the workload's)")
     ap.add_argument("--layout", choices=["bhtd", "bthd"], default="bhtd")
+    ap.add_argument("--kernel", choices=["auto", "vector", "mfma"], default="auto",
+                    help="decode kernel family (pa_kernel): auto picks matrix cores for grouped-query heads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device-to-device a few times (the known-size kernel that scales the "
+                         "HBM byte counters of a profiler run) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device copy of known size: each dispatch reads and writes exactly 1 GiB."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_dispatch": n, "bytes_written_per_dispatch": n,
+                                           "dispatches": 3}}), flush=True)
 
 
 def cpu_baseline(w, target_s):
@@ -100,6 +119,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.lib()                                                    # fail loudly if the library is missing
@@ -146,6 +168,7 @@ def main():
         f"KV bytes per decode call {kv_per_layer / 1e9:.4f} GB; workspace {ws_bytes} B")
 
     stream = torch.cuda.current_stream()
+    kern = {"auto": B.PA_KERNEL_AUTO, "vector": B.PA_KERNEL_VECTOR, "mfma": B.PA_KERNEL_MFMA}[args.kernel]
 
     def step(events=None):
         for li, (kc, vc, q, nk, nv, out) in enumerate(Ls):
@@ -153,7 +176,7 @@ def main():
             if events is not None:
                 events[2 * li].record(stream)
             B.pa_decode_ex(out, q, kc, vc, tables, ctx, w.scale, layout=layout, partition_tokens=pt,
-                           workspace=ws, stream=stream)
+                           kernel=kern, workspace=ws, stream=stream)
             if events is not None:
                 events[2 * li + 1].record(stream)
 
@@ -200,7 +223,7 @@ def main():
             "workload": f"{w.name}: {w.description}",
             "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "layers": layers,
-            "partition_tokens": pt, "layout": args.layout, "sum_context_tokens": int(w.context_lens.sum()),
+            "partition_tokens": pt, "layout": args.layout, "kernel": args.kernel, "sum_context_tokens": int(w.context_lens.sum()),
             "parallelism": "single GPU",
         },
         "seq_layers_per_s": round(seq_layers, 1),

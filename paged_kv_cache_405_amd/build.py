@@ -27,7 +27,11 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 # Packed FP32 VALU instructions are kept out of the generated code on purpose.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Matrix-core accumulators stay in ordinary VGPRs: the kernels rescale them
+# with vector ALU instructions, and with inline asm present the compiler would
+# otherwise hold them in AGPRs and copy them out and back on every tile.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"] + DEVICE_FLAGS
 

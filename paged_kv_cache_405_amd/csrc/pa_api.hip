@@ -42,7 +42,7 @@ struct Plan {
     bool mfma = false;          // grouped-query matrix-core kernel
     bool stream = false;        // balanced schedule (partition_tokens == 0)
     int n_waves = 0;            // stream: logical waves (one workgroup each)
-    size_t off_next = 0, off_ml = 0, off_acc = 0;   // stream: workspace sections
+    size_t off_first = 0, off_last = 0, off_ml = 0, off_acc = 0;   // stream: workspace sections
     int partition_blocks = 0;   // blocks per partition
     int max_partitions = 1;     // grid x extent
     int gt = 1;                 // q heads per workgroup
@@ -149,8 +149,10 @@ pa_status make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_di
         pl->max_partitions = 1;
         const size_t units = (size_t)num_seqs * num_kv_heads * pl->group_split;
         const size_t pieces = 2 * (size_t)pl->n_waves;
-        pl->off_next = round_up(units * sizeof(int32_t), WS_ALIGN);
-        pl->off_ml = pl->off_next + round_up(pieces * sizeof(int32_t), WS_ALIGN);
+        // [total steps T][unit_first][unit_last][piece max, sum][piece outputs]
+        pl->off_first = WS_ALIGN;
+        pl->off_last = pl->off_first + round_up(units * sizeof(int32_t), WS_ALIGN);
+        pl->off_ml = pl->off_last + round_up(units * sizeof(int32_t), WS_ALIGN);
         pl->off_acc = pl->off_ml + round_up(pieces * pl->gt * sizeof(float2), WS_ALIGN);
         pl->ws_bytes = pl->off_acc + pieces * pl->gt * (size_t)head_dim * sizeof(float);
         pl->ml_bytes = 0;
@@ -258,8 +260,9 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
     if (pl.stream) {
         char *ws = static_cast<char *>(workspace);
         p.n_waves = pl.n_waves;
-        p.unit_first = reinterpret_cast<int32_t *>(ws);
-        p.piece_next = reinterpret_cast<int32_t *>(ws + pl.off_next);
+        p.stream_total = reinterpret_cast<uint64_t *>(ws);
+        p.unit_first = reinterpret_cast<int32_t *>(ws + pl.off_first);
+        p.unit_last = reinterpret_cast<int32_t *>(ws + pl.off_last);
         p.piece_ml = reinterpret_cast<float2 *>(ws + pl.off_ml);
         p.piece_acc = reinterpret_cast<float *>(ws + pl.off_acc);
     } else if (pl.ws_bytes > 0) {

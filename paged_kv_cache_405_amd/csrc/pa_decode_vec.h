@@ -33,6 +33,10 @@
 
 namespace pa {
 
+#ifndef PA_VEC_STAGES
+#define PA_VEC_STAGES 2         // steps in the register pipeline of the vector kernel
+#endif
+
 // One wave's share of the work on one (sequence, kv head): the online-softmax
 // state of GT query heads and the step pipeline that feeds it.  A step is a
 // slab of NLD wave-wide loads of K and of V inside one (block, kv head) tile.
@@ -56,7 +60,12 @@ struct VecWorker {
     static constexpr int SLAB_TOK = NLD * ROWS;      // tokens per step
 
     static constexpr int STEP_TOK = SLAB_TOK;        // tokens per step of the schedule
+    static constexpr int LOADS_PER_TILE = 2 * NLD;   // vector-memory operations load() issues
+    static constexpr int LDS_BYTES = 0;              // no LDS staging
+    __device__ __forceinline__ void init_lds(unsigned char __attribute__((address_space(3))) *) {}
 
+    struct Buf;
+    __device__ __forceinline__ void bind_buf(Buf &, int) const {}
     struct Buf {
         uint4 k[NLD];
         uint4 v[NLD];
@@ -65,8 +74,9 @@ struct VecWorker {
 
     int seq, qh0;             // the unit bound to the worker: a sequence and GT q heads
     int chunk;                // this lane's 16-byte chunk of a row
-    const char *kb;           // K of this kv head at this lane's (row, chunk)
-    const char *vb;
+    const char *kpool;        // K of this kv head (wave-uniform)
+    const char *vpool;        // V of this kv head (wave-uniform)
+    int lane_off;             // this lane's (row, chunk) byte offset inside a slab
     const int32_t *trow;
     int64_t blk_bytes, ld_bytes;
     int num_blocks;
@@ -96,9 +106,9 @@ struct VecWorker {
             V::widen(ld16(static_cast<const char *>(P.q) + qi * ES), qf[g]);
         }
         const int row_c = row_on ? row : 0;
-        const int64_t lane_off = ((int64_t)kvh * P.head_stride + (int64_t)row_c * P.token_stride + chunk * VEC) * ES;
-        kb = static_cast<const char *>(P.k) + lane_off;
-        vb = static_cast<const char *>(P.v) + lane_off;
+        kpool = static_cast<const char *>(P.k) + (int64_t)kvh * P.head_stride * ES;
+        vpool = static_cast<const char *>(P.v) + (int64_t)kvh * P.head_stride * ES;
+        lane_off = (int)((int64_t)row_c * P.token_stride * ES) + chunk * 16;
         blk_bytes = P.block_stride * ES;
         ld_bytes = (int64_t)ROWS * P.token_stride * ES;
         trow = P.tables + (int64_t)s * P.max_blocks;
@@ -153,19 +163,31 @@ struct VecWorker {
     }
 
     // step q of the sequence: block q / NSLAB (a scalar load), slab q % NSLAB
-    __device__ __forceinline__ int phys(int q) const { return trow[q / NSLAB]; }
-
-    __device__ __forceinline__ void load(int q, int ph, Buf &b) const {
-        b.ok = (unsigned)ph < (unsigned)num_blocks;
-        const int64_t boff = (int64_t)(b.ok ? ph : 0) * blk_bytes + (int64_t)(q % NSLAB) * NLD * ld_bytes;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            b.k[i] = ld16(kb + boff + i * ld_bytes);
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            b.v[i] = ld16(vb + boff + i * ld_bytes);
+    __device__ __forceinline__ int2 tile_phys(int q) const {
+        const int ph = trow[q / NSLAB];
+        return make_int2(ph, ph);
     }
 
+    __device__ __forceinline__ void load(int q, int2 pp, Buf &b) const {
+        const int ph = pp.x;
+        b.ok = (unsigned)ph < (unsigned)num_blocks;
+        // slab base (wave-uniform) plus a 32-bit lane offset
+        const int64_t boff = (int64_t)(b.ok ? ph : 0) * blk_bytes + (int64_t)(q % NSLAB) * NLD * ld_bytes;
+        const char *ks = kpool + boff;
+        const char *vs = vpool + boff;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            b.k[i] = ld16(ks + i * ld_bytes + lane_off);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            b.v[i] = ld16(vs + i * ld_bytes + lane_off);
+    }
+
+    // the loads are the compiler's own: it places the waits
+    template <int BEHIND>
+    __device__ __forceinline__ void wait(Buf &) const {}
+
+    template <int BEHIND>
     __device__ __forceinline__ void compute(int q, const Buf &b) {
         const int t0 = q * SLAB_TOK;             // first token of the step
         // scores of this step, log2 units
@@ -235,31 +257,9 @@ struct VecWorker {
         }
     }
 
-    // steps qbeg, qbeg + stride, ... below qend (wave-uniform); same loop
-    // shape as the grouped-query kernel: pairs of steps, one back edge,
-    // unconditional next-step loads
+    // steps qbeg, qbeg + stride, ... below qend (wave-uniform)
     __device__ __forceinline__ void run(int qbeg, int qend, int stride) {
-        if (qbeg >= qend)
-            return;
-        const int n = (qend - 1 - qbeg) / stride + 1;
-        const int qlast = qbeg + (n - 1) * stride;
-        Buf b0, b1;
-        int q = qbeg;
-        load(q, phys(q), b0);
-        int pn = phys(min(q + stride, qlast));
-        for (int it = 1; it < n; it += 2) {
-            load(min(q + stride, qlast), pn, b1);
-            pn = phys(min(q + 2 * stride, qlast));
-            __builtin_amdgcn_sched_barrier(0);   // next loads go out before this step's math
-            compute(q, b0);
-            load(min(q + 2 * stride, qlast), pn, b0);
-            pn = phys(min(q + 3 * stride, qlast));
-            __builtin_amdgcn_sched_barrier(0);
-            compute(q + stride, b1);
-            q += 2 * stride;
-        }
-        if (n & 1)
-            compute(q, b0);
+        pipeline<PA_VEC_STAGES>(*this, qbeg, qend, stride);
     }
 
     // merge the token rows of the wave (lanes that differ in the row bits)
@@ -405,11 +405,18 @@ __global__ __launch_bounds__(64) void reduce_kernel(const DecodeParams P)
         L = fmaf(v.y, fast_exp2(v.x - M), L);
     }
     L = group_sum<64>(L);
-    for (int d = lane; d < D; d += 64) {
-        float A = 0.f;
-        for (int i = 0; i < npart; ++i)
-            A = fmaf(acc[(int64_t)i * D + d], fast_exp2(ml[i].x - M), A);
-        Store<T>::one(P.out, sh * D + d, L > 0.f ? A / L : 0.f);
+    // the partitions' loads do not depend on one another: unrolled, several
+    // are in flight at once
+#pragma unroll
+    for (int d0 = 0; d0 < D; d0 += 64) {
+        const int d = d0 + lane;
+        if (d < D) {
+            float A = 0.f;
+#pragma unroll 4
+            for (int i = 0; i < npart; ++i)
+                A = fmaf(acc[(int64_t)i * D + d], fast_exp2(ml[i].x - M), A);
+            Store<T>::one(P.out, sh * D + d, L > 0.f ? A / L : 0.f);
+        }
     }
 }
 

@@ -191,6 +191,90 @@ struct TableWindow {
 };
 
 // ---------------------------------------------------------------------------
+// The tile pipeline shared by the decode workers.  A worker W provides
+//   W::Buf                          registers of one tile's K and V loads
+//   int2 W::tile_phys(int k)        physical block(s) of tile k (scalar loads)
+//   void W::load(int k, int2, Buf&) issue tile k's loads
+//   void W::wait<B>(Buf&)           wait until the tile's register loads have
+//                                   landed, B = tiles issued after it
+//   void W::compute<B>(int k, Buf&) the tile's math
+//   W::LOADS_PER_TILE               vector-memory operations load() issues
+// and pipeline<STAGES>() runs tiles kbeg, kbeg + stride, ... below kend (all
+// wave-uniform) with STAGES buffers in rotation: while tile k is computed,
+// the loads of the next STAGES-1 tiles are in flight.  The loop runs over
+// groups of STAGES tiles with one back edge and issues every load
+// unconditionally (past the end it reloads the last tile, never used), so
+// the wait before a tile's math is the same on every path and step: that
+// tile's loads, never those issued behind it.  The last n % STAGES tiles
+// follow in straight-line code that issues no loads, so there the count of
+// loads behind a tile falls by one tile per step.  Every buffer that was
+// loaded is waited for exactly once, on every path, whether its tile is
+// computed or not: a load whose result the compiler thought unused would
+// leave its registers free for other values while the load is still in
+// flight.  Table entries are fetched one load ahead, as scalar loads,
+// counted apart from the vector loads.
+// ---------------------------------------------------------------------------
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding and leaves the other counters alone (gfx9 encoding:
+// vmcnt[3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+    return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
+}
+
+// tail step I of pipeline(): buffer I has the loads of the STAGES - 2 - I
+// buffers after it behind it
+template <int STAGES, int I, class W, class B>
+__device__ __forceinline__ void pipeline_tail(W &w, B (&b)[STAGES], int kt, int stride, int left)
+{
+    if constexpr (I < STAGES - 1) {
+        w.template wait<STAGES - 2 - I>(b[I]);
+        if (I < left)
+            w.template compute<STAGES - 2 - I>(kt + I * stride, b[I]);
+        pipeline_tail<STAGES, I + 1>(w, b, kt, stride, left);
+    }
+}
+
+template <int STAGES, class W>
+__device__ __forceinline__ void pipeline(W &w, int kbeg, int kend, int stride)
+{
+    static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
+    kbeg = __builtin_amdgcn_readfirstlane(kbeg);
+    kend = __builtin_amdgcn_readfirstlane(kend);
+    stride = __builtin_amdgcn_readfirstlane(stride);
+    if (kbeg >= kend)
+        return;
+    const int n = (kend - 1 - kbeg) / stride + 1;   // tiles of this wave
+    const int klast = kbeg + (n - 1) * stride;
+    typename W::Buf b[STAGES];
+#pragma unroll
+    for (int i = 0; i < STAGES; ++i)
+        w.bind_buf(b[i], i);
+    int2 pn = w.tile_phys(kbeg);
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i) {
+        w.load(min(kbeg + i * stride, klast), pn, b[i]);
+        pn = w.tile_phys(min(kbeg + (i + 1) * stride, klast));
+    }
+    int kt = kbeg;
+    int it = 0;
+    for (; it + STAGES <= n; it += STAGES) {
+#pragma unroll
+        for (int i = 0; i < STAGES; ++i) {
+            w.load(min(kt + (i + STAGES - 1) * stride, klast), pn, b[(i + STAGES - 1) % STAGES]);
+            pn = w.tile_phys(min(kt + (i + STAGES) * stride, klast));
+            __builtin_amdgcn_sched_barrier(0);   // the loads go out before this tile's math
+            w.template wait<STAGES - 1>(b[i]);
+            w.template compute<STAGES - 1>(kt + i * stride, b[i]);
+        }
+        kt += STAGES * stride;
+    }
+    pipeline_tail<STAGES, 0>(w, b, kt, stride, n - it);
+    // retire every load still in flight (direct-to-LDS loads of unused
+    // reloads included) before any LDS slot is reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // launch parameters
 // ---------------------------------------------------------------------------
 struct DecodeParams {
@@ -218,8 +302,9 @@ struct DecodeParams {
     // balanced (stream) schedule: waves take equal shares of the step stream of
     // all (head group, sequence) units; a unit cut between waves leaves pieces
     int n_waves;              // logical waves of the stream kernel (a multiple of 8)
+    uint64_t *stream_total;   // [1] steps of the whole stream (T), written by the stream kernel
     int32_t *unit_first;      // [HG * S] first piece of each unit, -1 when one wave finished it
-    int32_t *piece_next;      // [2 * n_waves] next piece of the same unit, -1 after the last
+    int32_t *unit_last;       // [HG * S] last piece of each cut unit
     float2 *piece_ml;         // [2 * n_waves][heads per unit] (max in log2 units, sum)
     float *piece_acc;         // [2 * n_waves][heads per unit][D] unnormalised partial outputs
 };

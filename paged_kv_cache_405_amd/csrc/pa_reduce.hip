@@ -44,12 +44,14 @@ hipError_t launch_reduce(const DecodeParams &p, int dtype, int head_dim, int blo
 template <typename T>
 static hipError_t launch_stream_reduce_t(const DecodeParams &p, int head_dim, int heads_per_unit, hipStream_t st)
 {
-    dim3 grid(p.num_seqs, p.num_kv_heads * p.group_split);
+    if (heads_per_unit < 1 || heads_per_unit > 65535)
+        return hipErrorInvalidValue;
+    dim3 grid(p.num_seqs, p.num_kv_heads * p.group_split, heads_per_unit);
     switch (head_dim) {
-    case 32: hipLaunchKernelGGL((stream_reduce_kernel<T, 32>), grid, dim3(128), 0, st, p, heads_per_unit); break;
-    case 64: hipLaunchKernelGGL((stream_reduce_kernel<T, 64>), grid, dim3(128), 0, st, p, heads_per_unit); break;
-    case 128: hipLaunchKernelGGL((stream_reduce_kernel<T, 128>), grid, dim3(128), 0, st, p, heads_per_unit); break;
-    case 256: hipLaunchKernelGGL((stream_reduce_kernel<T, 256>), grid, dim3(128), 0, st, p, heads_per_unit); break;
+    case 32: hipLaunchKernelGGL((stream_reduce_kernel<T, 32>), grid, dim3(64), 0, st, p, heads_per_unit); break;
+    case 64: hipLaunchKernelGGL((stream_reduce_kernel<T, 64>), grid, dim3(64), 0, st, p, heads_per_unit); break;
+    case 128: hipLaunchKernelGGL((stream_reduce_kernel<T, 128>), grid, dim3(64), 0, st, p, heads_per_unit); break;
+    case 256: hipLaunchKernelGGL((stream_reduce_kernel<T, 256>), grid, dim3(64), 0, st, p, heads_per_unit); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -34,12 +34,19 @@
 
 namespace pa {
 
+// a value that is the same in every lane, as a scalar (uniform) value
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // wave-wide sum and inclusive prefix sum of a 64-bit value
 __device__ __forceinline__ int64_t wave_sum64(int64_t x) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1)
         x += __shfl_xor(x, off);
-    return x;
+    return uniform64(x);
 }
 __device__ __forceinline__ int64_t wave_incl_scan64(int64_t x, int lane) {
 #pragma unroll
@@ -57,15 +64,20 @@ __device__ __forceinline__ uint64_t range_start(int w, uint64_t T, int N) {
     return q * (uint64_t)w + (r * (uint64_t)w) / (uint64_t)N;
 }
 
-// logical wave whose range holds position c (c < T): the largest w with
-// range_start(w) <= c, i.e. floor(((c + 1) N - 1) / T)
-__device__ __forceinline__ int wave_of(uint64_t c, uint64_t T, int N) {
-    const unsigned __int128 x = (unsigned __int128)(c + 1) * (unsigned)N - 1;
-    return (int)(x / T);
-}
+#ifndef PA_STREAM_SEQ_MAJOR
+#define PA_STREAM_SEQ_MAJOR 0      // 1: units ordered sequence major (all head groups of a sequence together)
+#endif
+#ifndef PA_STREAM_XCD_MAJOR
+#define PA_STREAM_XCD_MAJOR 1      // 1: logical waves assigned XCD major
+#endif
+
+#ifndef PA_STREAM_WAVES_PER_EU
+#define PA_STREAM_WAVES_PER_EU 1   // waves per SIMD the register allocation must allow (1 = no limit)
+#endif
 
 template <class W, int BS>
-__global__ __launch_bounds__(64) void decode_stream_kernel(const DecodeParams P)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_STREAM_WAVES_PER_EU)))
+void decode_stream_kernel(const DecodeParams P)
 {
     constexpr int STEP = W::STEP_TOK;
     const int lane = threadIdx.x;
@@ -84,38 +96,57 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const DecodeParams P)
     }
     const uint64_t T = (uint64_t)tseq * (uint64_t)HG;
     const int bid = blockIdx.x;
-    const int w = (bid & 7) * (N >> 3) + (bid >> 3);
+    const int w = PA_STREAM_XCD_MAJOR ? (bid & 7) * (N >> 3) + (bid >> 3) : bid;
+    if (bid == 0 && lane == 0)
+        P.stream_total[0] = T;
     const uint64_t c_lo = range_start(w, T, N);
     const uint64_t c_hi = range_start(w + 1, T, N);
     if (c_lo >= c_hi)
         return;
 
-    // locate c_lo: head group, then the sequence by a prefix scan, then the step
-    int hg = (int)(c_lo / (uint64_t)tseq);
+    // locate c_lo: the sequence by a prefix scan over the units' step counts
+    // (times HG when the head groups of a sequence are consecutive), then the
+    // head group and the step
+    constexpr bool SEQ_MAJOR = PA_STREAM_SEQ_MAJOR != 0;
+    int hg = SEQ_MAJOR ? 0 : (int)(c_lo / (uint64_t)tseq);
     const int64_t r0 = (int64_t)(c_lo - (uint64_t)hg * (uint64_t)tseq);
+    const int64_t mult = SEQ_MAJOR ? HG : 1;
     int s = 0;
     int64_t base = 0;
     for (int b = 0; b < S; b += 64) {
         const int i = b + lane;
-        const int64_t n = i < S ? max(1, (clamp_ctx(P.ctx[i]) + STEP - 1) / STEP) : 0;
+        const int64_t n = i < S ? mult * max(1, (clamp_ctx(P.ctx[i]) + STEP - 1) / STEP) : 0;
         const int64_t incl = wave_incl_scan64(n, lane);
         const int64_t tot = __shfl(incl, 63);
         if (r0 < base + tot) {
             const uint64_t hit = __ballot(i < S && base + incl > r0);
             const int k = __ffsll((unsigned long long)hit) - 1;
-            s = b + k;
-            base += __shfl(incl - n, k);
+            s = __builtin_amdgcn_readfirstlane(b + k);
+            base += uniform64(__shfl(incl - n, k));
             break;
         }
-        base += tot;
+        base += uniform64(tot);
     }
-    int j = (int)(r0 - base);
+    int64_t rj = r0 - base;
+    if (SEQ_MAJOR) {
+        const int ns = max(1, (clamp_ctx(P.ctx[s]) + STEP - 1) / STEP);
+        hg = (int)(rj / ns);
+        rj -= (int64_t)hg * ns;
+    }
+    int j = __builtin_amdgcn_readfirstlane((int)rj);
 
     W wk;
     wk.init_lane(lane);
+    __shared__ __attribute__((aligned(16))) unsigned char lds[W::LDS_BYTES > 0 ? W::LDS_BYTES : 16];
+    wk.init_lds((unsigned char __attribute__((address_space(3))) *)lds);
     uint64_t pos = c_lo;
     bool first = true;
     for (;;) {
+        // the cursor is the same in every lane; say so, so that addresses
+        // derived from it (table row, tile indices) stay scalar
+        s = __builtin_amdgcn_readfirstlane(s);
+        hg = __builtin_amdgcn_readfirstlane(hg);
+        j = __builtin_amdgcn_readfirstlane(j);
         const int ctx = clamp_ctx(P.ctx[s]);
         const int nreal = (ctx + STEP - 1) / STEP;
         const int nsched = max(1, nreal);
@@ -135,7 +166,8 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const DecodeParams P)
             if (lane == 0) {
                 if (j == 0)
                     P.unit_first[u] = piece;
-                P.piece_next[piece] = jend == nsched ? -1 : 2 * wave_of(pos + (uint64_t)(jend - j), T, N);
+                if (jend == nsched)
+                    P.unit_last[u] = piece;
             }
         }
         pos += (uint64_t)(jend - j);
@@ -143,44 +175,88 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const DecodeParams P)
             break;
         first = false;
         j = 0;
-        if (++s == S) {
+        if (SEQ_MAJOR) {
+            if (++hg == HG) {
+                hg = 0;
+                ++s;
+            }
+        } else if (++s == S) {
             s = 0;
             ++hg;
         }
     }
 }
 
-// Merge the pieces of every unit the stream kernel cut: one workgroup per
-// unit (grid x = sequence, y = head group), threads over (head, dim).
+// Merge the pieces of every unit the stream kernel cut: one wave per (unit,
+// head of the unit), grid x = sequence, y = head group, z = head.  The piece
+// list is known from its two ends, so no load waits on another: first the
+// reference max over the pieces (lanes over pieces), then the rescaled sums
+// (lanes over dims).
 template <typename T, int D>
-__global__ __launch_bounds__(128) void stream_reduce_kernel(const DecodeParams P, int heads_per_unit)
+__global__ __launch_bounds__(64) void stream_reduce_kernel(const DecodeParams P, int heads_per_unit)
 {
     const int s = blockIdx.x;
     const int hg = blockIdx.y;
-    const int first = P.unit_first[(int64_t)hg * P.num_seqs + s];
+    const int g = blockIdx.z;
+    const int64_t u = (int64_t)hg * P.num_seqs + s;
+    const int first = P.unit_first[u];
     if (first < 0)
         return;
-    const int kvh = hg / P.group_split;
-    const int qh0 = kvh * P.group + (hg - kvh * P.group_split) * heads_per_unit;
-    const int max_pieces = 2 * P.n_waves;
-    for (int idx = threadIdx.x; idx < heads_per_unit * D; idx += blockDim.x) {
-        const int g = idx / D;
-        const int d = idx - g * D;
-        float M = NEG_BIG, L = 0.f, A = 0.f;
-        int p = first;
-        for (int it = 0; p >= 0 && it < max_pieces; ++it) {
-            const float2 ml = P.piece_ml[(int64_t)p * heads_per_unit + g];
-            const float a = P.piece_acc[((int64_t)p * heads_per_unit + g) * D + d];
-            const float mn = fmaxf(M, ml.x);
-            const float c0 = fast_exp2(M - mn);
-            const float c1 = fast_exp2(ml.x - mn);
-            L = L * c0 + ml.y * c1;
-            A = A * c0 + a * c1;
-            M = mn;
-            p = P.piece_next[p];
+    const int w0 = first >> 1;
+    const int w1 = P.unit_last[u] >> 1;   // the last piece is 2 w1
+    const uint64_t total = P.stream_total[0];
+    const int N = P.n_waves;
+    const bool every_wave = total >= (uint64_t)N;   // then no range is empty
+    auto empty = [&](int w) {
+        return !every_wave && w > w0 && range_start(w, total, N) == range_start(w + 1, total, N);
+    };
+    auto slot = [&](int w) { return (int64_t)(w == w0 ? first : 2 * w) * heads_per_unit + g; };
+
+    const int lane = threadIdx.x;
+    // the reference max: one piece per lane, 64 at a time
+    float M = NEG_BIG;
+    for (int w = w0 + lane; w <= w1; w += 64)
+        if (!empty(w))
+            M = fmaxf(M, P.piece_ml[slot(w)].x);
+    M = group_max<64>(M);
+
+    // each lane weighs one piece of a round of 64, then the wave adds the
+    // round's outputs dim by dim with those weights
+    constexpr int E = (D + 63) / 64;
+    float A[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        A[e] = 0.f;
+    float L = 0.f;
+    for (int base = w0; base <= w1; base += 64) {
+        const int w = base + lane;
+        float c = 0.f;
+        if (w <= w1 && !empty(w)) {
+            const float2 ml = P.piece_ml[slot(w)];
+            c = fast_exp2(ml.x - M);
+            L = fmaf(ml.y, c, L);
         }
-        Store<T>::one(P.out, ((int64_t)s * P.num_q_heads + qh0 + g) * D + d, L > 0.f ? A / L : 0.f);
+        const int cnt = min(64, w1 - base + 1);
+#pragma unroll 4
+        for (int i = 0; i < cnt; ++i) {
+            if (empty(base + i))
+                continue;
+            const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), i));
+            const float *a = P.piece_acc + slot(base + i) * D;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (lane + 64 * e < D)
+                    A[e] = fmaf(a[lane + 64 * e], ci, A[e]);
+        }
     }
+    L = group_sum<64>(L);
+    const int kvh = hg / P.group_split;
+    const int qh = kvh * P.group + (hg - kvh * P.group_split) * heads_per_unit + g;
+    const int64_t o = ((int64_t)s * P.num_q_heads + qh) * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (lane + 64 * e < D)
+            Store<T>::one(P.out, o + lane + 64 * e, L > 0.f ? A[e] / L : 0.f);
 }
 
 template <class W, int BS>
