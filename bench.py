@@ -42,7 +42,7 @@ def parse():
                     choices=["llama7b", "llama70b_gqa", "mixed_bs8", "mixed_bs16", "mixed_bs32", "shared_prefix"])
     ap.add_argument("--layers", type=int, default=None, help="default: 32 (7B-shaped), 80 (70B-shaped)")
     ap.add_argument("--partition-tokens", type=int, default=None,
-                    help="0 = library's choice, -1 = single pass, N = split-K partition (default: the workload's)")
+                    help="0 = library's choice (default), -1 = single pass, -2 = balanced schedule, N = split-K partition of N tokens")
     ap.add_argument("--layout", choices=["bhtd", "bthd"], default="bhtd")
     ap.add_argument("--kernel", choices=["auto", "vector", "mfma"], default="auto",
                     help="decode kernel family (pa_kernel): auto picks matrix cores for grouped-query heads")
@@ -129,7 +129,8 @@ def main():
     w = W.WORKLOADS[args.workload](poison=False)
     layers = args.layers or (80 if w.num_q_heads == 64 else 32)
     layout = B.PA_LAYOUT_BHTD if args.layout == "bhtd" else B.PA_LAYOUT_BTHD
-    pt = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    # the library's own choice unless a partition is asked for
+    pt = B.PA_PARTITION_AUTO if args.partition_tokens is None else args.partition_tokens
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     log(f"[bench] workload {w.name}: {w.description}; layers {layers}; partition {pt}; layout {args.layout}")
 
@@ -169,6 +170,18 @@ def main():
 
     stream = torch.cuda.current_stream()
     kern = {"auto": B.PA_KERNEL_AUTO, "vector": B.PA_KERNEL_VECTOR, "mfma": B.PA_KERNEL_MFMA}[args.kernel]
+    dtype_code = {"f32": B.PA_F32, "f16": B.PA_F16, "bf16": B.PA_BF16}[w.dtype]
+    # the path the library resolves the automatic choices to
+    path_pt, path_kern = B.pa_decode_path(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                          w.max_blocks_per_seq, dtype_code, pt, kern)
+    family = "mfma" if path_kern == B.PA_KERNEL_MFMA else "vec"
+    if path_pt == B.PA_PARTITION_BALANCED:
+        path_name, call_kernels = "balanced", f"decode_stream_kernel ({family}) + stream_reduce_kernel"
+    elif path_pt == B.PA_PARTITION_SINGLE:
+        path_name, call_kernels = "single", f"decode_{family}_kernel"
+    else:
+        path_name, call_kernels = f"split-K {path_pt} tokens", f"decode_{family}_kernel + reduce_kernel"
+    log(f"[bench] path: {path_name}, kernels per call: {call_kernels}")
 
     def step(events=None):
         for li, (kc, vc, q, nk, nv, out) in enumerate(Ls):
@@ -202,6 +215,12 @@ def main():
     log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms (wall {wall * 1e3:.3f} ms); "
         f"decode call avg {avg_call_ms * 1e3:.2f} us, median {statistics.median(call_ms) * 1e3:.2f} us")
 
+    # HBM bytes per call from the committed counter record, when it was taken
+    # on these kernel sources (else null)
+    from paged_kv_cache_405_amd import traffic as TR
+    rec = TR.lookup(args.workload, path_pt, path_kern, args.layout)
+    traffic_bytes = None if rec is None else int(round(rec["bytes_per_call"]))
+    traffic_source = None if rec is None else "profiles/hbm_traffic.json (rocprofv3 FETCH_SIZE, WRITE_SIZE)"
     calls = args.steps * layers
     kv_gbs = kv_per_layer * calls / (total_ms * 1e-3) / 1e9
     achieved = kv_per_layer / (avg_call_ms * 1e-3) / 1e9
@@ -223,20 +242,22 @@ def main():
             "workload": f"{w.name}: {w.description}",
             "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "layers": layers,
-            "partition_tokens": pt, "layout": args.layout, "kernel": args.kernel, "sum_context_tokens": int(w.context_lens.sum()),
+            "partition_tokens": pt, "layout": args.layout, "kernel": args.kernel,
+            "path": {"partition": path_name, "kernel_family": family}, "sum_context_tokens": int(w.context_lens.sum()),
             "parallelism": "single GPU",
         },
         "seq_layers_per_s": round(seq_layers, 1),
         "hbm_peak_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
         "kv_bytes_per_layer": kv_per_layer,
         "roofline": {
-            "kernel": "pa_decode call (decode kernel + split-K reduce kernel when partitioned)",
+            "kernel": f"pa_decode call: {call_kernels}",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic_bytes,
+            "traffic_source": traffic_source,
             "avg_call_us": round(avg_call_ms * 1e3, 3),
             "bytes_per_call": kv_per_layer,
         },

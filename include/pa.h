@@ -103,6 +103,26 @@ typedef enum pa_kernel {
     PA_KERNEL_MFMA = 2
 } pa_kernel;
 
+/*
+ * How the tokens of one sequence are split across workgroups (the
+ * partition_tokens argument of pa_decode_ex; a positive value N is a split-K
+ * partition of N tokens, see there).
+ *
+ *   PA_PARTITION_AUTO      the library picks: a single pass when the
+ *                          (sequence, kv head) units number at least four per
+ *                          compute unit -- the hardware then balances whole
+ *                          units over the device -- else the balanced schedule.
+ *   PA_PARTITION_SINGLE    one workgroup reads a whole context; no workspace.
+ *   PA_PARTITION_BALANCED  every wave of the device reads the same number of
+ *                          tokens: contexts are cut wherever the shares end,
+ *                          and a reduce kernel merges the cut units' pieces.
+ */
+typedef enum pa_partition {
+    PA_PARTITION_AUTO = 0,
+    PA_PARTITION_SINGLE = -1,
+    PA_PARTITION_BALANCED = -2
+} pa_partition;
+
 /* Supported shapes: head_dim in {32, 64, 128, 256}; block_size in {8, 16, 32};
  * any num_q_heads that is a multiple of num_kv_heads. */
 
@@ -146,11 +166,11 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
  *   num_blocks        blocks in the pool; a table entry outside [0, num_blocks)
  *                     contributes no tokens instead of being read
  *   layout            PA_LAYOUT_BHTD or PA_LAYOUT_BTHD
- *   partition_tokens  0  = the library picks (split-K for long contexts);
- *                     -1 = single pass, one workgroup reads a whole context;
- *                     N > 0 = each workgroup reads at most N tokens of one
- *                     sequence (N a multiple of block_size) and a reduce kernel
- *                     merges the partitions' (max, sum, partial output).
+ *   partition_tokens  PA_PARTITION_AUTO (0), PA_PARTITION_SINGLE (-1),
+ *                     PA_PARTITION_BALANCED (-2) (above), or N > 0: each
+ *                     workgroup reads at most N tokens of one sequence (N a
+ *                     multiple of block_size) and a reduce kernel merges the
+ *                     partitions' (max, sum, partial output).
  *   kernel            PA_KERNEL_AUTO, PA_KERNEL_VECTOR or PA_KERNEL_MFMA (above)
  *
  * Per-block partial results are combined with a running max and sum
@@ -164,8 +184,21 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pa_decode_path -- the path pa_decode_ex takes for these sizes, with the
+ * automatic choices resolved: *partition_out receives PA_PARTITION_SINGLE,
+ * PA_PARTITION_BALANCED or the partition in tokens, *kernel_out
+ * PA_KERNEL_VECTOR or PA_KERNEL_MFMA.  Arguments and errors as for
+ * pa_decode_ex (PA_ERR_INVALID_ARG for a null output pointer); the automatic
+ * partition and the balanced schedule query the current device.  Nothing is
+ * launched.
+ */
+pa_status pa_decode_path(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                         int max_blocks_per_seq, pa_dtype dtype, int partition_tokens, pa_kernel kernel,
+                         int *partition_out, pa_kernel *kernel_out);
+
+/*
  * pa_decode_workspace_bytes -- bytes of workspace pa_decode / pa_decode_ex
- * need for these sizes and this partition_tokens (0, -1 or N, as above).
+ * need for these sizes and this partition_tokens (0, -1, -2 or N, as above).
  * Writes 0 when the call runs single pass.  Returns the same status the
  * decode call would return for these sizes.
  */

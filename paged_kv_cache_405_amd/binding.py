@@ -24,6 +24,7 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = ra
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_LAYOUT_BHTD, PA_LAYOUT_BTHD = 0, 1
 PA_KERNEL_AUTO, PA_KERNEL_VECTOR, PA_KERNEL_MFMA = 0, 1, 2
+PA_PARTITION_AUTO, PA_PARTITION_SINGLE, PA_PARTITION_BALANCED = 0, -1, -2
 STATUS_NAMES = {PA_OK: "PA_OK", PA_ERR_INVALID_ARG: "PA_ERR_INVALID_ARG", PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED",
                 PA_ERR_WORKSPACE: "PA_ERR_WORKSPACE", PA_ERR_HIP: "PA_ERR_HIP"}
 
@@ -60,6 +61,8 @@ def lib():
             L.pa_decode_ex.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, i32, i32, vp, sz, vp]
             L.pa_decode_workspace_bytes.restype = i32
             L.pa_decode_workspace_bytes.argtypes = [i32] * 8 + [ctypes.POINTER(sz)]
+            L.pa_decode_path.restype = i32
+            L.pa_decode_path.argtypes = [i32] * 9 + [ctypes.POINTER(i32), ctypes.POINTER(i32)]
             L.pa_reshape_and_cache.restype = i32
             L.pa_reshape_and_cache.argtypes = [vp] * 5 + [i32] * 7 + [vp]
             L.pa_status_string.restype = ctypes.c_char_p
@@ -126,6 +129,17 @@ def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, blo
     if st != PA_OK:
         raise PaError(st, "pa_decode_workspace_bytes")
     return int(out.value)
+
+
+def pa_decode_path(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                   dtype_code, partition_tokens=0, kernel=PA_KERNEL_AUTO) -> tuple[int, int]:
+    """(partition, kernel) pa_decode_ex resolves these arguments to."""
+    part, kern = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = lib().pa_decode_path(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                              dtype_code, partition_tokens, kernel, ctypes.byref(part), ctypes.byref(kern))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_path")
+    return int(part.value), int(kern.value)
 
 
 def _workspace(q, nbytes, workspace):

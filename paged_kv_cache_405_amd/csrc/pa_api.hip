@@ -37,6 +37,7 @@ bool mfma_shape(pa_dtype dtype, int head_dim, int group)
 // Smallest q-head group the library sends to the matrix cores on its own:
 // below it the per-token vector work is small enough for the VALU.
 constexpr int MFMA_MIN_GROUP = 4;
+constexpr long long AUTO_UNITS_PER_CU = 4;   // single pass at or above this many units per compute unit
 
 struct Plan {
     bool mfma = false;          // grouped-query matrix-core kernel
@@ -60,7 +61,7 @@ pa_status check_sizes(int num_seqs, int num_q_heads, int num_kv_heads, int head_
         return PA_ERR_INVALID_ARG;
     if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
         return PA_ERR_UNSUPPORTED;
-    if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % block_size != 0))
+    if (partition_tokens < PA_PARTITION_BALANCED || (partition_tokens > 0 && partition_tokens % block_size != 0))
         return PA_ERR_INVALID_ARG;
     if ((long long)max_blocks_per_seq * block_size > (1LL << 30))
         return PA_ERR_UNSUPPORTED;
@@ -118,23 +119,34 @@ pa_status make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_di
     if (kernel == PA_KERNEL_MFMA && !mfma_ok)
         return PA_ERR_UNSUPPORTED;
     pl->mfma = kernel == PA_KERNEL_MFMA || (kernel == PA_KERNEL_AUTO && mfma_ok && group >= MFMA_MIN_GROUP);
-    const int pt = partition_tokens;
+    if (pl->mfma)
+        pl->gt = group <= 16 ? group : 16;
+    else
+        pl->gt = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    pl->group_split = group / pl->gt;
+    int pt = partition_tokens;
+    if (pt == PA_PARTITION_AUTO) {
+        // enough (sequence, head group) units that whole units, handed out by
+        // the hardware as workgroups finish, keep every compute unit busy:
+        // one pass, no reduce; else cut contexts into equal shares
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return PA_ERR_HIP;
+        const long long units = (long long)num_seqs * num_kv_heads * pl->group_split;
+        pt = units >= AUTO_UNITS_PER_CU * (long long)cus ? PA_PARTITION_SINGLE : PA_PARTITION_BALANCED;
+    }
     const long long max_tokens = (long long)block_size * max_blocks_per_seq;
-    if (pt <= 0 || pt >= max_tokens) {      // balanced schedule (0) or single pass
+    if (pt <= 0 || pt >= max_tokens) {      // balanced schedule or single pass
         pl->partition_blocks = max_blocks_per_seq;
         pl->max_partitions = 1;
     } else {
         pl->partition_blocks = pt / block_size;
         pl->max_partitions = (max_blocks_per_seq + pl->partition_blocks - 1) / pl->partition_blocks;
     }
-    if (pl->mfma)
-        pl->gt = group <= 16 ? group : 16;
-    else
-        pl->gt = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
-    pl->group_split = group / pl->gt;
     if ((long long)num_kv_heads * pl->group_split > 65535 || num_seqs > 65535)
         return PA_ERR_UNSUPPORTED;
-    if (partition_tokens == 0) {
+    if (pt == PA_PARTITION_BALANCED) {
         // balanced schedule: as many one-wave workgroups as the device holds at
         // once (a multiple of 8, one share per XCD), pieces for cut units
         int cus = 0;
@@ -187,6 +199,23 @@ int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
 }  // namespace
 
 extern "C" {
+
+pa_status pa_decode_path(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                         int max_blocks_per_seq, pa_dtype dtype, int partition_tokens, pa_kernel kernel,
+                         int *partition_out, pa_kernel *kernel_out)
+{
+    if (!partition_out || !kernel_out)
+        return PA_ERR_INVALID_ARG;
+    Plan pl;
+    const pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, dtype, partition_tokens, kernel, &pl);
+    if (st != PA_OK)
+        return st;
+    *partition_out = pl.stream ? PA_PARTITION_BALANCED
+                   : pl.max_partitions > 1 ? pl.partition_blocks * block_size : PA_PARTITION_SINGLE;
+    *kernel_out = pl.mfma ? PA_KERNEL_MFMA : PA_KERNEL_VECTOR;
+    return PA_OK;
+}
 
 pa_status pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                     int block_size, int max_blocks_per_seq, pa_dtype dtype,
@@ -375,6 +404,6 @@ const char *pa_status_string(pa_status status)
     }
 }
 
-int pa_abi_version(void) { return 100; }
+int pa_abi_version(void) { return 101; }
 
 }  // extern "C"

@@ -192,6 +192,8 @@ void decode_stream_kernel(const DecodeParams P)
 // list is known from its two ends, so no load waits on another: first the
 // reference max over the pieces (lanes over pieces), then the rescaled sums
 // (lanes over dims).
+constexpr int FEW_PIECES = 16;   // pieces per unit the reduce merges in one batch of loads
+
 template <typename T, int D>
 __global__ __launch_bounds__(64) void stream_reduce_kernel(const DecodeParams P, int heads_per_unit)
 {
@@ -213,43 +215,65 @@ __global__ __launch_bounds__(64) void stream_reduce_kernel(const DecodeParams P,
     auto slot = [&](int w) { return (int64_t)(w == w0 ? first : 2 * w) * heads_per_unit + g; };
 
     const int lane = threadIdx.x;
-    // the reference max: one piece per lane, 64 at a time
-    float M = NEG_BIG;
-    for (int w = w0 + lane; w <= w1; w += 64)
-        if (!empty(w))
-            M = fmaxf(M, P.piece_ml[slot(w)].x);
-    M = group_max<64>(M);
-
-    // each lane weighs one piece of a round of 64, then the wave adds the
-    // round's outputs dim by dim with those weights
     constexpr int E = (D + 63) / 64;
     float A[E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
         A[e] = 0.f;
     float L = 0.f;
-    for (int base = w0; base <= w1; base += 64) {
-        const int w = base + lane;
-        float c = 0.f;
-        if (w <= w1 && !empty(w)) {
-            const float2 ml = P.piece_ml[slot(w)];
-            c = fast_exp2(ml.x - M);
-            L = fmaf(ml.y, c, L);
-        }
-        const int cnt = min(64, w1 - base + 1);
-#pragma unroll 4
-        for (int i = 0; i < cnt; ++i) {
-            if (empty(base + i))
-                continue;
-            const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), i));
-            const float *a = P.piece_acc + slot(base + i) * D;
+    const int np = w1 - w0 + 1;
+    if (every_wave && np <= FEW_PIECES) {
+        // the usual case: every load of the merge goes out at once -- each
+        // lane's (max, sum) of piece `lane` and the outputs of all pieces
+        const float2 ml = lane < np ? P.piece_ml[slot(w0 + lane)] : make_float2(NEG_BIG, 0.f);
+        float a[FEW_PIECES][E];
+#pragma unroll
+        for (int i = 0; i < FEW_PIECES; ++i)
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                if (lane + 64 * e < D)
-                    A[e] = fmaf(a[lane + 64 * e], ci, A[e]);
+                a[i][e] = i < np && lane + 64 * e < D ? P.piece_acc[slot(w0 + i) * D + lane + 64 * e] : 0.f;
+        const float M = group_max<64>(ml.x);
+        const float c = fast_exp2(ml.x - M);
+        L = group_sum<64>(ml.y * c);
+#pragma unroll
+        for (int i = 0; i < FEW_PIECES; ++i) {
+            const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), i));
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                A[e] = fmaf(a[i][e], ci, A[e]);   // pieces past np hold 0
         }
+    } else {
+        // the reference max: one piece per lane, 64 at a time
+        float M = NEG_BIG;
+        for (int w = w0 + lane; w <= w1; w += 64)
+            if (!empty(w))
+                M = fmaxf(M, P.piece_ml[slot(w)].x);
+        M = group_max<64>(M);
+        // each lane weighs one piece of a round of 64, then the wave adds the
+        // round's outputs dim by dim with those weights
+        for (int base = w0; base <= w1; base += 64) {
+            const int w = base + lane;
+            float c = 0.f;
+            if (w <= w1 && !empty(w)) {
+                const float2 ml = P.piece_ml[slot(w)];
+                c = fast_exp2(ml.x - M);
+                L = fmaf(ml.y, c, L);
+            }
+            const int cnt = min(64, w1 - base + 1);
+#pragma unroll 4
+            for (int i = 0; i < cnt; ++i) {
+                if (empty(base + i))
+                    continue;
+                const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), i));
+                const float *a = P.piece_acc + slot(base + i) * D;
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (lane + 64 * e < D)
+                        A[e] = fmaf(a[lane + 64 * e], ci, A[e]);
+            }
+        }
+        L = group_sum<64>(L);
     }
-    L = group_sum<64>(L);
     const int kvh = hg / P.group_split;
     const int qh = kvh * P.group + (hg - kvh * P.group_split) * heads_per_unit + g;
     const int64_t o = ((int64_t)s * P.num_q_heads + qh) * D;

@@ -32,7 +32,7 @@ host_only = pytest.mark.skipif(not _no_gpu(), reason="fake device addresses are 
 def test_exports_every_declared_function(L):
     names = B.declared_functions()
     assert {"pa_decode", "pa_decode_ex", "pa_decode_workspace_bytes", "pa_reshape_and_cache",
-            "pa_status_string", "pa_abi_version"} <= set(names)
+            "pa_status_string", "pa_abi_version", "pa_decode_path"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in pa.h but not exported"
 
@@ -42,7 +42,7 @@ def test_status_strings_and_version(L):
         s = B.pa_status_string(code)
         assert isinstance(s, str) and s
     assert B.pa_status_string(99) == "unknown status"
-    assert B.pa_abi_version() == 100
+    assert B.pa_abi_version() == 101
 
 
 def _ws(S=4, Hq=8, Hkv=2, D=128, bs=16, MB=64, dt=B.PA_F16, pt=0):
@@ -65,10 +65,12 @@ def test_workspace_size_rules():
 
 @host_only
 def test_balanced_schedule_needs_a_device():
-    # partition_tokens = 0 sizes the balanced schedule for the current device:
-    # with none visible the query reports a HIP failure instead of guessing
-    assert _ws(MB=512, pt=0) == (B.PA_ERR_HIP, 0)
-    assert _decode(pt=0) == B.PA_ERR_HIP
+    # the balanced schedule is sized for the current device, and the
+    # automatic choice counts its compute units: with no device visible both
+    # report a HIP failure instead of guessing
+    for pt in (B.PA_PARTITION_AUTO, B.PA_PARTITION_BALANCED):
+        assert _ws(MB=512, pt=pt) == (B.PA_ERR_HIP, 0)
+        assert _decode(pt=pt) == B.PA_ERR_HIP
     # argument errors still come first, before any device query
     assert _decode(pt=0, q=None) == B.PA_ERR_INVALID_ARG
     assert _decode(pt=0, D=96) == B.PA_ERR_UNSUPPORTED
@@ -86,7 +88,7 @@ def test_balanced_schedule_needs_a_device():
     (dict(bs=1), B.PA_ERR_UNSUPPORTED),
     (dict(dt=3), B.PA_ERR_UNSUPPORTED),
     (dict(pt=24), B.PA_ERR_INVALID_ARG),
-    (dict(pt=-2), B.PA_ERR_INVALID_ARG),
+    (dict(pt=-3), B.PA_ERR_INVALID_ARG),
 ])
 def test_workspace_query_rejects(kw, status):
     assert _ws(**kw)[0] == status
@@ -171,3 +173,28 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(ImportError):
         B.lib()
+
+
+@host_only
+def test_decode_path_resolves_explicit_choices_without_a_device():
+    f16 = B.PA_F16
+    # explicit partition and kernel: no device query
+    assert B.pa_decode_path(4, 8, 8, 128, 16, 64, f16, B.PA_PARTITION_SINGLE, B.PA_KERNEL_VECTOR) == \
+        (B.PA_PARTITION_SINGLE, B.PA_KERNEL_VECTOR)
+    assert B.pa_decode_path(4, 8, 8, 128, 16, 64, f16, 256, B.PA_KERNEL_VECTOR) == (256, B.PA_KERNEL_VECTOR)
+    # a partition covering the whole table is a single pass
+    assert B.pa_decode_path(4, 8, 8, 128, 16, 64, f16, 1024, B.PA_KERNEL_VECTOR) == \
+        (B.PA_PARTITION_SINGLE, B.PA_KERNEL_VECTOR)
+    # the kernel family: matrix cores for groups of four or more q heads per kv head
+    assert B.pa_decode_path(4, 16, 2, 128, 16, 64, f16, -1, B.PA_KERNEL_AUTO)[1] == B.PA_KERNEL_MFMA
+    assert B.pa_decode_path(4, 4, 2, 128, 16, 64, f16, -1, B.PA_KERNEL_AUTO)[1] == B.PA_KERNEL_VECTOR
+    assert B.pa_decode_path(4, 16, 2, 128, 16, 64, B.PA_F32, -1, B.PA_KERNEL_AUTO)[1] == B.PA_KERNEL_VECTOR
+    # automatic partition needs the device
+    with pytest.raises(B.PaError):
+        B.pa_decode_path(4, 8, 8, 128, 16, 64, f16, B.PA_PARTITION_AUTO, B.PA_KERNEL_AUTO)
+    # null outputs and bad arguments
+    L = B.lib()
+    out = ctypes.c_int32(0)
+    assert L.pa_decode_path(4, 8, 8, 128, 16, 64, f16, -1, 0, None, ctypes.byref(out)) == B.PA_ERR_INVALID_ARG
+    assert L.pa_decode_path(4, 8, 8, 96, 16, 64, f16, -1, 0, ctypes.byref(out), ctypes.byref(out)) == \
+        B.PA_ERR_UNSUPPORTED

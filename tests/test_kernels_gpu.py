@@ -42,7 +42,7 @@ def test_mfma_kernel_ragged(dtype, D, bs, Hq, Hkv):
     g = upload(w)
     ref = oracle_step(w)
     first = True
-    for pt in (-1, 0, bs, 4 * bs, 256):
+    for pt in (-1, 0, -2, bs, 4 * bs, 256):
         out = gpu_step(w, g, partition_tokens=pt, append=first, kernel=B.PA_KERNEL_MFMA)
         first = False
         torch.cuda.synchronize()
@@ -67,7 +67,7 @@ def test_mfma_context_zero_and_one(dtype):
     """ctx = 0 gives a zero row; ctx = 1 gives V[0] bit for bit (p = 1, l = 1)."""
     w = W.custom(f"mfma_edge_{dtype}", dtype, [0, 1, 0, 1, 33], 16, 2, 128, 16, seed=15, append=False)
     g = upload(w)
-    for pt in (-1, 0, 16):
+    for pt in (-1, 0, -2, 16):
         out = gpu_step(w, g, partition_tokens=pt, append=False, kernel=B.PA_KERNEL_MFMA)
         torch.cuda.synchronize()
         got = out.cpu()

@@ -48,7 +48,7 @@ def test_workload_parity_default(cache, name):
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "llama7b", "mixed_bs8", "llama70b_gqa"])
-@pytest.mark.parametrize("pt", [0, -1, 16, 256, 512, 1024])
+@pytest.mark.parametrize("pt", [0, -1, -2, 16, 256, 512, 1024])
 def test_partitions(cache, name, pt):
     w = _workload(cache, name)
     if pt > 0 and pt % w.block_size:
@@ -94,7 +94,7 @@ def test_shapes_ragged(dtype, D, bs, Hq, Hkv):
                  seed=D * 7 + bs + Hq, append=True, table_pad=3)
     log(f"[gpu] {w.name}")
     g = upload(w)
-    for pt in (-1, 0, 4 * bs, 256):
+    for pt in (-1, 0, -2, 4 * bs, 256):
         out = gpu_step(w, g, partition_tokens=pt, append=(pt == -1))
         torch.cuda.synchronize()
         assert_close(compare(out, oracle_step(w), dtype), dtype, f"{w.name} pt={pt}")
@@ -106,7 +106,7 @@ def test_context_zero_and_one(dtype):
     w = W.custom(f"edge_{dtype}", dtype, [0, 1, 0, 1, 33], 4, 2, 128, 16, seed=5, append=False)
     log(f"[gpu] {w.name}")
     g = upload(w)
-    for pt in (-1, 0, 16):
+    for pt in (-1, 0, -2, 16):
         out = gpu_step(w, g, partition_tokens=pt, append=False)
         torch.cuda.synchronize()
         got = out.cpu()

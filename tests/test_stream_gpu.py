@@ -27,7 +27,7 @@ def test_one_long_sequence_cut_across_many_waves(dtype, kernel):
     w = W.custom(f"stream_long_{dtype}", dtype, [8191], 16, 2, 128, 16, seed=31, append=True)
     log(f"[gpu] {w.name} kernel {kernel}")
     g = upload(w)
-    out = gpu_step(w, g, partition_tokens=0, kernel=kernel)
+    out = gpu_step(w, g, partition_tokens=B.PA_PARTITION_BALANCED, kernel=kernel)
     torch.cuda.synchronize()
     assert_close(compare(out, oracle_step(w), dtype), dtype, f"{w.name} kernel={kernel}")
 
@@ -38,7 +38,7 @@ def test_empty_contexts_and_idle_waves(kernel):
     w = W.custom("stream_sparse", "bf16", ctxs, 8, 1, 128, 16, seed=32, append=False)
     log(f"[gpu] {w.name} kernel {kernel}")
     g = upload(w)
-    out = gpu_step(w, g, partition_tokens=0, append=False, kernel=kernel)
+    out = gpu_step(w, g, partition_tokens=B.PA_PARTITION_BALANCED, append=False, kernel=kernel)
     torch.cuda.synchronize()
     got = out.cpu()
     for s, c in enumerate(ctxs):
@@ -55,7 +55,7 @@ def test_vector_shapes_balanced(dtype, D, bs, Hq, Hkv):
                  seed=40 + D + bs, append=False, table_pad=1)
     log(f"[gpu] {w.name}")
     g = upload(w)
-    out = gpu_step(w, g, partition_tokens=0, append=False, kernel=B.PA_KERNEL_VECTOR)
+    out = gpu_step(w, g, partition_tokens=B.PA_PARTITION_BALANCED, append=False, kernel=B.PA_KERNEL_VECTOR)
     torch.cuda.synchronize()
     assert_close(compare(out, oracle_step(w, append=False), dtype), dtype, w.name)
 
@@ -65,9 +65,9 @@ def test_balanced_rerun_bit_identical(name):
     w = W.WORKLOADS[name]()
     log(f"[gpu] {name} balanced reruns")
     g = upload(w)
-    a = gpu_step(w, g, partition_tokens=0)
-    b = gpu_step(w, g, partition_tokens=0, append=False)
-    c = gpu_step(w, g, partition_tokens=0, append=False)
+    a = gpu_step(w, g, partition_tokens=B.PA_PARTITION_BALANCED)
+    b = gpu_step(w, g, partition_tokens=B.PA_PARTITION_BALANCED, append=False)
+    c = gpu_step(w, g, partition_tokens=B.PA_PARTITION_BALANCED, append=False)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
     assert_close(compare(a, oracle_step(w), w.dtype), w.dtype, f"{name} balanced")
