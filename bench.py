@@ -33,7 +33,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="0 = library's choice (default), -1 = single pass, -2 = balanced schedule, N = split-K partition of N tokens")
     ap.add_argument("--layout", choices=["bhtd", "bthd"], default="bhtd")
+    ap.add_argument("--shared-blocks", choices=["auto", "on", "off"], default="auto",
+                    help="PA_DECODE_SHARED_BLOCKS: auto = on when the workload's tables share blocks")
     ap.add_argument("--kernel", choices=["auto", "vector", "mfma"], default="auto",
                     help="decode kernel family (pa_kernel): auto picks matrix cores for grouped-query heads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -51,7 +53,7 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device a few times (the known-size kernel that scales the "
                          "HBM byte counters of a profiler run) and exit")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def copy_calibration():
@@ -105,6 +107,20 @@ def cpu_baseline(w, target_s):
     }
 
 
+def run_config(args, w, B):
+    """The host-side settings of a run (no device needed)."""
+    return {
+        "layers": args.layers or (80 if w.num_q_heads == 64 else 32),
+        "layout": B.PA_LAYOUT_BHTD if args.layout == "bhtd" else B.PA_LAYOUT_BTHD,
+        # the library's own choice unless a partition is asked for
+        "pt": B.PA_PARTITION_AUTO if args.partition_tokens is None else args.partition_tokens,
+        "kern": {"auto": B.PA_KERNEL_AUTO, "vector": B.PA_KERNEL_VECTOR, "mfma": B.PA_KERNEL_MFMA}[args.kernel],
+        "dtype_code": {"f32": B.PA_F32, "f16": B.PA_F16, "bf16": B.PA_BF16}[w.dtype],
+        # the caller knows when several sequences read the same blocks (a shared prefix)
+        "shared": args.shared_blocks == "on" or (args.shared_blocks == "auto" and w.shared_prefix_blocks > 0),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,10 +143,9 @@ def main():
     B.lib()                                                    # fail loudly if the library is missing
 
     w = W.WORKLOADS[args.workload](poison=False)
-    layers = args.layers or (80 if w.num_q_heads == 64 else 32)
-    layout = B.PA_LAYOUT_BHTD if args.layout == "bhtd" else B.PA_LAYOUT_BTHD
-    # the library's own choice unless a partition is asked for
-    pt = B.PA_PARTITION_AUTO if args.partition_tokens is None else args.partition_tokens
+    cfg = run_config(args, w, B)
+    layers, layout, pt, kern, shared, dtype_code = (cfg[k] for k in ("layers", "layout", "pt", "kern", "shared",
+                                                                        "dtype_code"))
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     log(f"[bench] workload {w.name}: {w.description}; layers {layers}; partition {pt}; layout {args.layout}")
 
@@ -169,8 +184,6 @@ def main():
         f"KV bytes per decode call {kv_per_layer / 1e9:.4f} GB; workspace {ws_bytes} B")
 
     stream = torch.cuda.current_stream()
-    kern = {"auto": B.PA_KERNEL_AUTO, "vector": B.PA_KERNEL_VECTOR, "mfma": B.PA_KERNEL_MFMA}[args.kernel]
-    dtype_code = {"f32": B.PA_F32, "f16": B.PA_F16, "bf16": B.PA_BF16}[w.dtype]
     # the path the library resolves the automatic choices to
     path_pt, path_kern = B.pa_decode_path(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
                                           w.max_blocks_per_seq, dtype_code, pt, kern)
@@ -189,7 +202,7 @@ def main():
             if events is not None:
                 events[2 * li].record(stream)
             B.pa_decode_ex(out, q, kc, vc, tables, ctx, w.scale, layout=layout, partition_tokens=pt,
-                           kernel=kern, workspace=ws, stream=stream)
+                           kernel=kern, shared_blocks=shared, workspace=ws, stream=stream)
             if events is not None:
                 events[2 * li + 1].record(stream)
 
@@ -218,7 +231,7 @@ def main():
     # HBM bytes per call from the committed counter record, when it was taken
     # on these kernel sources (else null)
     from paged_kv_cache_405_amd import traffic as TR
-    rec = TR.lookup(args.workload, path_pt, path_kern, args.layout)
+    rec = TR.lookup(args.workload, path_pt, path_kern, args.layout, shared)
     traffic_bytes = None if rec is None else int(round(rec["bytes_per_call"]))
     traffic_source = None if rec is None else "profiles/hbm_traffic.json (rocprofv3 FETCH_SIZE, WRITE_SIZE)"
     calls = args.steps * layers
@@ -243,7 +256,8 @@ def main():
             "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "layers": layers,
             "partition_tokens": pt, "layout": args.layout, "kernel": args.kernel,
-            "path": {"partition": path_name, "kernel_family": family}, "sum_context_tokens": int(w.context_lens.sum()),
+            "path": {"partition": path_name, "kernel_family": family},
+            "shared_blocks": shared, "sum_context_tokens": int(w.context_lens.sum()),
             "parallelism": "single GPU",
         },
         "seq_layers_per_s": round(seq_layers, 1),

@@ -123,6 +123,23 @@ typedef enum pa_partition {
     PA_PARTITION_BALANCED = -2
 } pa_partition;
 
+/*
+ * Flags of pa_decode_ex.
+ *
+ *   PA_DECODE_SHARED_BLOCKS  some physical blocks are read by more than one
+ *                            sequence in this call (a shared prompt prefix,
+ *                            parallel sampling, beams).  K and V are then
+ *                            loaded with the caches' normal policy, so that
+ *                            the later readers of a shared block find it in
+ *                            L2.  Without the flag every K/V row is loaded
+ *                            as read-once (the non-temporal hint), which
+ *                            streams faster from HBM but leaves no cached
+ *                            copy behind.  Results are identical either way.
+ */
+typedef enum pa_decode_flags {
+    PA_DECODE_SHARED_BLOCKS = 1
+} pa_decode_flags;
+
 /* Supported shapes: head_dim in {32, 64, 128, 256}; block_size in {8, 16, 32};
  * any num_q_heads that is a multiple of num_kv_heads. */
 
@@ -151,7 +168,8 @@ typedef enum pa_partition {
  *                  its content on entry does not matter
  *
  * Equivalent to pa_decode_ex with num_blocks = INT32_MAX (table entries are
- * trusted), layout PA_LAYOUT_BHTD, partition_tokens = 0 and PA_KERNEL_AUTO.
+ * trusted), layout PA_LAYOUT_BHTD, PA_PARTITION_AUTO, PA_KERNEL_AUTO and no
+ * flags (blocks are taken to be private to their sequence).
  */
 pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, const int32_t *context_lens,
@@ -172,6 +190,8 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
  *                     multiple of block_size) and a reduce kernel merges the
  *                     partitions' (max, sum, partial output).
  *   kernel            PA_KERNEL_AUTO, PA_KERNEL_VECTOR or PA_KERNEL_MFMA (above)
+ *   flags             0 or PA_DECODE_SHARED_BLOCKS (above); other bits are
+ *                     PA_ERR_INVALID_ARG
  *
  * Per-block partial results are combined with a running max and sum
  * ("online softmax"); the combine across partitions is the same operation.
@@ -181,7 +201,7 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                        int block_size, int max_blocks_per_seq, int num_blocks, float scale,
                        pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
-                       void *workspace, size_t workspace_bytes, void *stream);
+                       unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * pa_decode_path -- the path pa_decode_ex takes for these sizes, with the

@@ -25,6 +25,7 @@ PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_LAYOUT_BHTD, PA_LAYOUT_BTHD = 0, 1
 PA_KERNEL_AUTO, PA_KERNEL_VECTOR, PA_KERNEL_MFMA = 0, 1, 2
 PA_PARTITION_AUTO, PA_PARTITION_SINGLE, PA_PARTITION_BALANCED = 0, -1, -2
+PA_DECODE_SHARED_BLOCKS = 1
 STATUS_NAMES = {PA_OK: "PA_OK", PA_ERR_INVALID_ARG: "PA_ERR_INVALID_ARG", PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED",
                 PA_ERR_WORKSPACE: "PA_ERR_WORKSPACE", PA_ERR_HIP: "PA_ERR_HIP"}
 
@@ -58,7 +59,7 @@ def lib():
             L.pa_decode.restype = i32
             L.pa_decode.argtypes = [vp] * 6 + [i32] * 6 + [f32, i32, vp, sz, vp]
             L.pa_decode_ex.restype = i32
-            L.pa_decode_ex.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, i32, i32, vp, sz, vp]
+            L.pa_decode_ex.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, i32, i32, ctypes.c_uint32, vp, sz, vp]
             L.pa_decode_workspace_bytes.restype = i32
             L.pa_decode_workspace_bytes.argtypes = [i32] * 8 + [ctypes.POINTER(sz)]
             L.pa_decode_path.restype = i32
@@ -152,8 +153,12 @@ def _workspace(q, nbytes, workspace):
 
 
 def pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, *, num_blocks=None,
-                 layout=PA_LAYOUT_BHTD, partition_tokens=0, kernel=PA_KERNEL_AUTO, workspace=None, stream=None):
-    """out[S, Hq, D] <- paged decode attention of q[S, Hq, D] over the caches."""
+                 layout=PA_LAYOUT_BHTD, partition_tokens=0, kernel=PA_KERNEL_AUTO, shared_blocks=False,
+                 workspace=None, stream=None):
+    """out[S, Hq, D] <- paged decode attention of q[S, Hq, D] over the caches.
+
+    shared_blocks: some physical blocks are read by several sequences in this
+    call (PA_DECODE_SHARED_BLOCKS): keep them in the caches."""
     torch = _torch()
     code = _dtype_code(q)
     S, Hq, D = q.shape
@@ -169,7 +174,8 @@ def pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, *,
         _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
         S, Hq, Hkv, D, bs, MB, NB if num_blocks is None else int(num_blocks), float(scale), code, int(layout),
-        int(partition_tokens), int(kernel), None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream))
+        int(partition_tokens), int(kernel), PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
+        None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode_ex")
     return out

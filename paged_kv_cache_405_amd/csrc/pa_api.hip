@@ -248,8 +248,10 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                        int block_size, int max_blocks_per_seq, int num_blocks, float scale,
                        pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
-                       void *workspace, size_t workspace_bytes, void *stream)
+                       unsigned flags, void *workspace, size_t workspace_bytes, void *stream)
 {
+    if (flags & ~(unsigned)PA_DECODE_SHARED_BLOCKS)
+        return PA_ERR_INVALID_ARG;
     // argument checks (no HIP call), then the launch plan (which may query the
     // device for the balanced schedule), then the workspace
     pa_status st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
@@ -286,6 +288,7 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
     p.v = v_cache;
     p.tables = block_tables;
     p.ctx = context_lens;
+    p.kv_cached = (flags & PA_DECODE_SHARED_BLOCKS) ? 1 : 0;
     if (pl.stream) {
         char *ws = static_cast<char *>(workspace);
         p.n_waves = pl.n_waves;
@@ -354,7 +357,7 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
 {
     return pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, INT32_MAX, scale, dtype,
-                        PA_LAYOUT_BHTD, 0, PA_KERNEL_AUTO, workspace, workspace_bytes, stream);
+                        PA_LAYOUT_BHTD, PA_PARTITION_AUTO, PA_KERNEL_AUTO, 0u, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_cache,
@@ -404,6 +407,6 @@ const char *pa_status_string(pa_status status)
     }
 }
 
-int pa_abi_version(void) { return 101; }
+int pa_abi_version(void) { return 200; }
 
 }  // extern "C"

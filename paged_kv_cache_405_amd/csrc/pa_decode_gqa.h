@@ -125,18 +125,27 @@ typedef unsigned int gqa_u32x4 __attribute__((ext_vector_type(4)));
 // for all of them.  Vector-memory loads return in issue order, so the waits
 // below count exactly: a tile's K is in registers once at most `n` loads
 // issued after it are still in flight, and likewise its V in LDS.
+template <bool NT>
 __device__ __forceinline__ gqa_u32x4 load_k_asm(const char *p, int off_bytes) {
     gqa_u32x4 r;
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p + off_bytes) : "memory");
+    if constexpr (NT)
+        asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p + off_bytes) : "memory");
+    else
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p + off_bytes) : "memory");
     return r;
 }
 // M0 carries the LDS destination of a direct load; the clobber tells the
 // compiler it changed (it warns that M0 is reserved, which is the point)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
 __device__ __forceinline__ void load_lds_asm(const char *src, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(lds_addr) : "m0", "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+                     :: "v"(src), "s"(lds_addr) : "m0", "memory");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                     :: "v"(src), "s"(lds_addr) : "m0", "memory");
 }
 #pragma clang diagnostic pop
 // wait for the K loads of one tile: the registers are operands of the
@@ -156,19 +165,27 @@ __device__ __forceinline__ void vm_wait_tied(gqa_u32x4 (&k)[8]) {
 // The same two loads with the address split into a wave-uniform 64-bit base
 // (scalar registers) and a 32-bit per-lane offset: no vector arithmetic per
 // load.  Usable when a tile's 16 rows lie in one block.
-template <int OFF>
+template <int OFF, bool NT>
 __device__ __forceinline__ gqa_u32x4 load_k_sbase(const char *base, uint32_t voff) {
     gqa_u32x4 r;
-    asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3" : "=v"(r) : "v"(voff), "s"(base), "i"(OFF) : "memory");
+    if constexpr (NT)
+        asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3 nt" : "=v"(r) : "v"(voff), "s"(base), "i"(OFF) : "memory");
+    else
+        asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3" : "=v"(r) : "v"(voff), "s"(base), "i"(OFF) : "memory");
     return r;
 }
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // no instruction offset here: on a load into LDS it moves the LDS
 // destination as well as the source, so the whole offset goes into the base
+template <bool NT>
 __device__ __forceinline__ void load_lds_sbase(const char *base, uint32_t voff, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(base), "s"(lds_addr) : "m0", "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                     :: "v"(voff), "s"(base), "s"(lds_addr) : "m0", "memory");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(voff), "s"(base), "s"(lds_addr) : "m0", "memory");
 }
 #pragma clang diagnostic pop
 
@@ -223,7 +240,7 @@ __device__ __forceinline__ void lgkm_wait_tied(gqa_u32x2 (&v)[16]) {
                  :: "memory");
 }
 
-template <typename T, int D, int BS>
+template <typename T, int D, int BS, bool STREAM_KV>
 struct GqaWorker {
     static constexpr int ES = 2;
     static constexpr int NC = D / 32;           // score MFMAs per tile
@@ -331,7 +348,7 @@ struct GqaWorker {
     template <int C = 0>
     __device__ __forceinline__ void load_k_rows(const char *base, Buf &b) const {
         if constexpr (C < NC) {
-            b.k[C] = load_k_sbase<32 * C * ES>(base, (uint32_t)k_lane);
+            b.k[C] = load_k_sbase<32 * C * ES, STREAM_KV>(base, (uint32_t)k_lane);
             load_k_rows<C + 1>(base, b);
         }
     }
@@ -340,7 +357,7 @@ struct GqaWorker {
         if constexpr (I < NL) {
             constexpr int grp = I / (D / 128);        // token group: tokens 4 grp .. 4 grp + 3
             constexpr int half = I % (D / 128);       // which 128 dims
-            load_lds_sbase(base + (int64_t)(4 * grp) * tok_bytes + 256 * half, (uint32_t)v_src, slot + I * LOAD_LDS);
+            load_lds_sbase<STREAM_KV>(base + (int64_t)(4 * grp) * tok_bytes + 256 * half, (uint32_t)v_src, slot + I * LOAD_LDS);
             load_v_rows<I + 1>(base, slot);
         }
     }
@@ -364,7 +381,7 @@ struct GqaWorker {
             const char *ka = lr >= BS ? bb : ba;
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                b.k[c] = load_k_asm(ka, k_lane + 32 * c * ES);
+                b.k[c] = load_k_asm<STREAM_KV>(ka, k_lane + 32 * c * ES);
             const char *va = (b.oka ? vpool + (int64_t)pp.x * blk_bytes : vpool) + row0;
             const char *vb = (b.okb ? vpool + (int64_t)pp.y * blk_bytes : vpool) + row0;
 #pragma unroll
@@ -372,7 +389,7 @@ struct GqaWorker {
                 const int grp = i / (D / 128);
                 const int half = i % (D / 128);
                 const char *src = 4 * grp >= BS ? vb - (int64_t)BS * tok_bytes : va;
-                load_lds_asm(src + (int64_t)(4 * grp) * tok_bytes + (v_src + 256 * half), slot + i * LOAD_LDS);
+                load_lds_asm<STREAM_KV>(src + (int64_t)(4 * grp) * tok_bytes + (v_src + 256 * half), slot + i * LOAD_LDS);
             }
         }
     }

@@ -17,12 +17,12 @@ namespace pa {
 // Grid schedule (partition_tokens != 0): one workgroup of NW waves per
 // (partition, head group, sequence); the waves take the partition's tiles
 // round robin and merge through LDS, reusing the tile slots.
-template <typename T, int D, int BS, int NW>
+template <typename T, int D, int BS, int NW, bool STREAM_KV>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams P)
 {
     static_assert(D % 128 == 0, "the grouped-query kernel needs head_dim 128 or 256");
     static_assert(BS % 8 == 0, "block size 8, 16 or 32");
-    using W = GqaWorker<T, D, BS>;
+    using W = GqaWorker<T, D, BS, STREAM_KV>;
     constexpr int MERGE_BYTES = NW * 16 * (D + 2) * 4;
     constexpr int LDS_TOTAL = NW * W::LDS_BYTES > MERGE_BYTES ? NW * W::LDS_BYTES : MERGE_BYTES;
 
@@ -101,7 +101,10 @@ template <typename T, int D, int BS>
 hipError_t launch_mfma_shape(const DecodeParams &p, hipStream_t st)
 {
     dim3 grid(p.max_partitions, p.num_kv_heads * p.group_split, p.num_seqs);
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, BS, MFMA_WAVES>), grid, dim3(MFMA_WAVES * 64), 0, st, p);
+    if (p.kv_cached)
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, BS, MFMA_WAVES, false>), grid, dim3(MFMA_WAVES * 64), 0, st, p);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, BS, MFMA_WAVES, true>), grid, dim3(MFMA_WAVES * 64), 0, st, p);
     return hipGetLastError();
 }
 
@@ -131,12 +134,13 @@ hipError_t launch_mfma_dtype(const DecodeParams &p, int head_dim, int bs, hipStr
 template <typename T, int D, int BS>
 hipError_t mfma_stream_shape(const DecodeParams *p, hipStream_t st, int *occ)
 {
-    using W = GqaWorker<T, D, BS>;
+    // the two load policies compile to the same registers: the occupancy of one is that of both
     if (occ) {
-        *occ = stream_occupancy<W, BS>();
+        *occ = stream_occupancy<GqaWorker<T, D, BS, true>, BS>();
         return hipSuccess;
     }
-    return launch_stream<W, BS>(*p, st);
+    return p->kv_cached ? launch_stream<GqaWorker<T, D, BS, false>, BS>(*p, st)
+                        : launch_stream<GqaWorker<T, D, BS, true>, BS>(*p, st);
 }
 
 template <typename T>

@@ -44,7 +44,7 @@ namespace pa {
 // alternate, the next step's loads are issued unconditionally before the
 // current step's math, and block-table entries are wave-uniform scalar loads
 // fetched one step further ahead.
-template <typename T, int D, int BS, int GT>
+template <typename T, int D, int BS, int GT, bool STREAM_KV>
 struct VecWorker {
     using V = Vec<T>;
     static constexpr int VEC = V::N;                 // elements per 16 bytes
@@ -177,10 +177,10 @@ struct VecWorker {
         const char *vs = vpool + boff;
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
-            b.k[i] = ld16(ks + i * ld_bytes + lane_off);
+            b.k[i] = ld16_kv<STREAM_KV>(ks + i * ld_bytes + lane_off);
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
-            b.v[i] = ld16(vs + i * ld_bytes + lane_off);
+            b.v[i] = ld16_kv<STREAM_KV>(vs + i * ld_bytes + lane_off);
     }
 
     // the loads are the compiler's own: it places the waits
@@ -283,10 +283,10 @@ struct VecWorker {
     }
 };
 
-template <typename T, int D, int BS, int GT, int NW>
+template <typename T, int D, int BS, int GT, int NW, bool STREAM_KV>
 __global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams P)
 {
-    using W = VecWorker<T, D, BS, GT>;
+    using W = VecWorker<T, D, BS, GT, STREAM_KV>;
     constexpr int VEC = W::VEC;
 
     const int p = blockIdx.x;
@@ -429,7 +429,10 @@ template <typename T, int D, int BS, int GT>
 hipError_t launch_decode_shape(const DecodeParams &p, hipStream_t st)
 {
     dim3 grid(p.max_partitions, p.num_kv_heads * p.group_split, p.num_seqs);
-    hipLaunchKernelGGL((decode_vec_kernel<T, D, BS, GT, DECODE_WAVES>), grid, dim3(DECODE_WAVES * 64), 0, st, p);
+    if (p.kv_cached)
+        hipLaunchKernelGGL((decode_vec_kernel<T, D, BS, GT, DECODE_WAVES, false>), grid, dim3(DECODE_WAVES * 64), 0, st, p);
+    else
+        hipLaunchKernelGGL((decode_vec_kernel<T, D, BS, GT, DECODE_WAVES, true>), grid, dim3(DECODE_WAVES * 64), 0, st, p);
     return hipGetLastError();
 }
 
@@ -473,12 +476,13 @@ hipError_t launch_decode_dtype(const DecodeParams &p, int head_dim, int bs, int 
 template <typename T, int D, int BS, int GT>
 hipError_t vec_stream_shape(const DecodeParams *p, hipStream_t st, int *occ)
 {
-    using W = VecWorker<T, D, BS, GT>;
+    // the two load policies compile to the same registers: the occupancy of one is that of both
     if (occ) {
-        *occ = stream_occupancy<W, BS>();
+        *occ = stream_occupancy<VecWorker<T, D, BS, GT, true>, BS>();
         return hipSuccess;
     }
-    return launch_stream<W, BS>(*p, st);
+    return p->kv_cached ? launch_stream<VecWorker<T, D, BS, GT, false>, BS>(*p, st)
+                        : launch_stream<VecWorker<T, D, BS, GT, true>, BS>(*p, st);
 }
 
 template <typename T, int D, int BS>

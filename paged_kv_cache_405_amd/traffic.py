@@ -10,7 +10,7 @@ and build flags: once they change, the measurement no longer describes the
 code and ``lookup`` returns None.
 
     python -m paged_kv_cache_405_amd.traffic record --workload llama7b \\
-        --partition -1 --kernel 1 --layout bhtd \\
+        --partition -1 --kernel 1 --layout bhtd [--shared-blocks] \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --command "rocprofv3 ..." [--command ...]
 
@@ -69,8 +69,12 @@ def _copy_kib(dirname: str, counter: str) -> float:
     return max(per.values())
 
 
-def record(path, workload, partition, kernel, layout, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir,
-           commands):
+def _key(r):
+    return (r["workload"], r["partition"], r["kernel"], r["layout"], r.get("shared_blocks", False))
+
+
+def record(path, workload, partition, kernel, layout, shared_blocks, fetch_dir, write_dir, copy_fetch_dir,
+           copy_write_dir, commands):
     fetch = _decode_kernels(_counter(fetch_dir, "FETCH_SIZE"))
     write = _decode_kernels(_counter(write_dir, "WRITE_SIZE"))
     fetch_scale = COPY_BYTES / 1024 / _copy_kib(copy_fetch_dir, "FETCH_SIZE")
@@ -82,6 +86,7 @@ def record(path, workload, partition, kernel, layout, fetch_dir, write_dir, copy
     write_bytes = sum(v["WRITE_SIZE_kib"] for v in kernels.values()) * 1024 * write_scale
     entry = {
         "workload": workload, "partition": int(partition), "kernel": int(kernel), "layout": layout,
+        "shared_blocks": bool(shared_blocks),
         "sources_sha256": sources_digest(),
         "fetch_scale": fetch_scale, "write_scale": write_scale,
         "kernels": kernels,
@@ -93,16 +98,14 @@ def record(path, workload, partition, kernel, layout, fetch_dir, write_dir, copy
     if os.path.exists(path):
         with open(path) as fh:
             data = json.load(fh)
-    key = (workload, int(partition), int(kernel), layout)
-    data["records"] = [r for r in data["records"]
-                       if (r["workload"], r["partition"], r["kernel"], r["layout"]) != key] + [entry]
+    data["records"] = [r for r in data["records"] if _key(r) != _key(entry)] + [entry]
     with open(path, "w") as fh:
         json.dump(data, fh, indent=1, sort_keys=True)
         fh.write("\n")
     return entry
 
 
-def lookup(workload, partition, kernel, layout, path=DEFAULT_PATH):
+def lookup(workload, partition, kernel, layout, shared_blocks=False, path=DEFAULT_PATH):
     """The record for this configuration if it was measured on the current sources, else None."""
     if not os.path.exists(path):
         return None
@@ -110,7 +113,7 @@ def lookup(workload, partition, kernel, layout, path=DEFAULT_PATH):
         data = json.load(fh)
     digest = sources_digest()
     for r in data.get("records", []):
-        if (r["workload"], r["partition"], r["kernel"], r["layout"]) == (workload, partition, kernel, layout):
+        if _key(r) == (workload, partition, kernel, layout, bool(shared_blocks)):
             return r if r["sources_sha256"] == digest else None
     return None
 
@@ -124,14 +127,15 @@ def main():
     r.add_argument("--partition", type=int, required=True)
     r.add_argument("--kernel", type=int, required=True)
     r.add_argument("--layout", default="bhtd")
+    r.add_argument("--shared-blocks", action="store_true")
     r.add_argument("--fetch", required=True)
     r.add_argument("--write", required=True)
     r.add_argument("--copy-fetch", required=True)
     r.add_argument("--copy-write", required=True)
     r.add_argument("--command", action="append", default=[])
     a = ap.parse_args()
-    e = record(a.path, a.workload, a.partition, a.kernel, a.layout, a.fetch, a.write, a.copy_fetch,
-               a.copy_write, a.command)
+    e = record(a.path, a.workload, a.partition, a.kernel, a.layout, a.shared_blocks, a.fetch, a.write,
+               a.copy_fetch, a.copy_write, a.command)
     print(json.dumps({k: e[k] for k in ("workload", "partition", "kernel", "bytes_per_call", "read_bytes_per_call",
                                         "write_bytes_per_call", "fetch_scale", "write_scale")}))
 

@@ -69,6 +69,7 @@ class Workload:
     new_v: Optional[np.ndarray] = None
     slot_mapping: Optional[np.ndarray] = None  # [T] int64
     description: str = ""
+    shared_prefix_blocks: int = 0              # leading blocks every table shares (0: blocks are private)
 
     @property
     def num_seqs(self): return self.q.shape[0]
@@ -175,7 +176,7 @@ def _finish(name, dtype, rng, q_shape, ctx, bs, Hkv, D, MB, poison, append, scal
     k, v = _fill_pool(rng, NB, bs, Hkv, D, dtype, tables, ctx, poison)
     w = Workload(name=name, dtype=dtype, q=q, k_cache=k, v_cache=v, block_tables=tables,
                  context_lens=ctx, scale=float(np.float32(scale)), partition_tokens=partition_tokens,
-                 description=description)
+                 description=description, shared_prefix_blocks=int(shared_prefix_blocks or 0))
     if append:
         w.new_k, w.new_v, w.slot_mapping = _take_appended(k, v, tables, ctx, bs, poison, dtype)
     return w

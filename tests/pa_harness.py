@@ -89,13 +89,14 @@ def upload(w: Workload, layout=B.PA_LAYOUT_BHTD) -> GpuInputs:
 
 
 def gpu_step(w: Workload, g: GpuInputs, partition_tokens=0, append=True, num_blocks=None,
-             kernel=B.PA_KERNEL_AUTO) -> torch.Tensor:
+             kernel=B.PA_KERNEL_AUTO, shared_blocks=False) -> torch.Tensor:
     """Append (if the workload has new tokens) then decode, on the current stream."""
     if append and g.slots is not None:
         B.pa_reshape_and_cache(g.new_k, g.new_v, g.k_cache, g.v_cache, g.slots, layout=g.layout)
     out = torch.empty_like(g.q)
     B.pa_decode_ex(out, g.q, g.k_cache, g.v_cache, g.tables, g.ctx, w.scale, layout=g.layout,
-                   partition_tokens=partition_tokens, num_blocks=num_blocks, kernel=kernel)
+                   partition_tokens=partition_tokens, num_blocks=num_blocks, kernel=kernel,
+                   shared_blocks=shared_blocks)
     return out
 
 

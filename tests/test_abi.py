@@ -42,7 +42,7 @@ def test_status_strings_and_version(L):
         s = B.pa_status_string(code)
         assert isinstance(s, str) and s
     assert B.pa_status_string(99) == "unknown status"
-    assert B.pa_abi_version() == 101
+    assert B.pa_abi_version() == 200
 
 
 def _ws(S=4, Hq=8, Hkv=2, D=128, bs=16, MB=64, dt=B.PA_F16, pt=0):
@@ -103,11 +103,12 @@ FAKE = 0x7f0000000000   # 16-byte aligned, never dereferenced
 
 def _decode(**kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, S=2, Hq=4, Hkv=2, D=64, bs=16, MB=8, NB=32,
-             scale=0.125, dt=B.PA_F16, layout=B.PA_LAYOUT_BHTD, pt=-1, kern=B.PA_KERNEL_AUTO, ws=None, wsb=0)
+             scale=0.125, dt=B.PA_F16, layout=B.PA_LAYOUT_BHTD, pt=-1, kern=B.PA_KERNEL_AUTO, flags=0, ws=None,
+             wsb=0)
     a.update(kw)
     return B.lib().pa_decode_ex(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["Hq"], a["Hkv"],
                                 a["D"], a["bs"], a["MB"], a["NB"], a["scale"], a["dt"], a["layout"], a["pt"],
-                                a["kern"], a["ws"], a["wsb"], None)
+                                a["kern"], a["flags"], a["ws"], a["wsb"], None)
 
 
 def test_empty_batch_is_a_noop():
@@ -198,3 +199,9 @@ def test_decode_path_resolves_explicit_choices_without_a_device():
     assert L.pa_decode_path(4, 8, 8, 128, 16, 64, f16, -1, 0, None, ctypes.byref(out)) == B.PA_ERR_INVALID_ARG
     assert L.pa_decode_path(4, 8, 8, 96, 16, 64, f16, -1, 0, ctypes.byref(out), ctypes.byref(out)) == \
         B.PA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("flags", [2, 4, 0x80000000])
+def test_decode_rejects_unknown_flags(flags):
+    # checked before anything else, so no device is needed to see it
+    assert _decode(flags=flags) == B.PA_ERR_INVALID_ARG

@@ -190,3 +190,18 @@ def test_placement_and_rerun_bit_identical(cache, name):
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("kernel", [B.PA_KERNEL_VECTOR, B.PA_KERNEL_MFMA])
+@pytest.mark.parametrize("pt", [B.PA_PARTITION_SINGLE, B.PA_PARTITION_BALANCED, 64])
+def test_shared_blocks_flag_changes_no_bit(kernel, pt):
+    # PA_DECODE_SHARED_BLOCKS only changes the cache policy of the K/V loads:
+    # on tables that share a prefix, both settings match the oracle and each other bit for bit
+    w = W.shared_prefix(seed=41, num_seqs=12)
+    g = upload(w)
+    log(f"[gpu] shared prefix flag kernel {kernel} pt {pt}")
+    a = gpu_step(w, g, partition_tokens=pt, kernel=kernel, shared_blocks=True)
+    b = gpu_step(w, g, partition_tokens=pt, kernel=kernel, shared_blocks=False, append=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert_close(compare(a, oracle_step(w), w.dtype), w.dtype, f"shared blocks kernel={kernel} pt={pt}")

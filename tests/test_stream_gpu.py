@@ -77,8 +77,9 @@ def test_workspace_exact_size():
     w = W.custom("stream_ws", "f16", [100, 2000, 7], 32, 8, 128, 16, seed=33, append=False)
     g = upload(w)
     S, Hq, D = w.q.shape
-    need = B.pa_decode_workspace_bytes(S, Hq, w.num_kv_heads, D, w.block_size, w.max_blocks_per_seq, B.PA_F16, 0)
-    # unit heads, piece links, (max, sum) pairs and partial outputs of at least 8 waves
+    bal = B.PA_PARTITION_BALANCED
+    need = B.pa_decode_workspace_bytes(S, Hq, w.num_kv_heads, D, w.block_size, w.max_blocks_per_seq, B.PA_F16, bal)
+    # (max, sum) pairs and partial outputs of the two piece slots of at least 8 waves
     assert need >= 2 * 8 * (4 + 8 + D * 4)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(g.q)
@@ -86,7 +87,7 @@ def test_workspace_exact_size():
     args = lambda nbytes: (out.data_ptr(), g.q.data_ptr(), g.k_cache.data_ptr(), g.v_cache.data_ptr(),  # noqa: E731
                            g.tables.data_ptr(), g.ctx.data_ptr(), S, Hq, w.num_kv_heads, D, w.block_size,
                            w.max_blocks_per_seq, w.num_blocks, ctypes.c_float(w.scale), B.PA_F16, B.PA_LAYOUT_BHTD,
-                           0, B.PA_KERNEL_AUTO, ws.data_ptr(), nbytes, ctypes.c_void_p(
+                           bal, B.PA_KERNEL_AUTO, 0, ws.data_ptr(), nbytes, ctypes.c_void_p(
                                torch.cuda.current_stream().cuda_stream))
     assert L.pa_decode_ex(*args(need - 1)) == B.PA_ERR_WORKSPACE
     assert L.pa_decode_ex(*args(need)) == B.PA_OK
