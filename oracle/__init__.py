@@ -1,5 +1,8 @@
 """CPU oracle for paged decode attention -- TEST INFRASTRUCTURE ONLY.
 
+``oracle.blocks`` holds the block bookkeeping (tables, reference counts,
+copy on write, swapping) and the block copies, as plain Python and numpy.
+
 Only the tests, the smoke check and the CPU-baseline leg of ``bench.py`` may
 import this package.  The GPU library and its Python binding never do.
 """
