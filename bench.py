@@ -50,10 +50,105 @@ def parse(argv=None):
                     help="decode kernel family (pa_kernel): auto picks matrix cores for grouped-query heads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=["decode", "copy_blocks", "swap_out", "swap_in"], default="decode",
+                    help="decode (the default step) or one of the block moves of the paging system: copy_blocks "
+                         "(copy on write inside the GPU pools), swap_out / swap_in (GPU pools <-> pinned host pools)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device a few times (the known-size kernel that scales the "
                          "HBM byte counters of a profiler run) and exit")
     return ap.parse_args(argv)
+
+
+HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def block_moves(args):
+    """Time one of the block moves on Llama-2-7B-shaped blocks (32 kv heads x 16 tokens x 128, fp16:
+    128 KiB of K and of V per block): copy on write of 1024 blocks inside 8192-block GPU pools, or
+    swapping 256 blocks between those pools and 2048-block pinned host pools."""
+    import torch
+    from paged_kv_cache_405_amd import binding as B
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+    bs, Hkv, D = 16, 32, 128
+    NG, NC = 8192, 2048
+    n = 1024 if args.op == "copy_blocks" else 256
+    block_bytes = bs * Hkv * D * 2
+    rng = np.random.default_rng(11)
+    gk = torch.randn((NG, Hkv, bs, D), device=dev, dtype=torch.float16)
+    gv = torch.randn_like(gk)
+    if args.op == "copy_blocks":
+        perm = rng.permutation(NG)
+        pairs = np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int32)
+        ck = cv = None
+    else:
+        ck = torch.empty((NC, Hkv, bs, D), dtype=torch.float16).pin_memory()
+        cv = torch.empty_like(ck).pin_memory()
+        ck.normal_()
+        cv.normal_()
+        g, c = rng.permutation(NG)[:n], rng.permutation(NC)[:n]
+        pairs = np.stack([g, c] if args.op == "swap_out" else [c, g], 1).astype(np.int32)
+    dpairs = torch.from_numpy(pairs).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        if args.op == "copy_blocks":
+            B.copy_blocks(gk, gv, dpairs, stream=stream)
+        elif args.op == "swap_out":
+            B.swap_blocks(ck, cv, gk, gv, dpairs, stream=stream)
+        else:
+            B.swap_blocks(gk, gv, ck, cv, dpairs, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    call_ms = statistics.fmean(a.elapsed_time(b) for a, b in evs)
+    moved = 2 * n * block_bytes                      # K and V blocks
+    if args.op == "copy_blocks":
+        bound, peak, algo = "hbm", HBM_PEAK_GBS, 2 * moved     # read and write, both in HBM
+    else:
+        bound, peak, algo = "host-link", HOST_LINK_PEAK_GBS, moved   # each byte crosses the link once
+    achieved = algo / (call_ms * 1e-3) / 1e9
+    # the oracle's copy (numpy, as it is) on a bounded sample of the same blocks
+    from oracle.blocks import copy_blocks as oracle_copy
+    sample = 64
+    hk = np.random.default_rng(1).standard_normal((sample * 2, Hkv, bs, D)).astype(np.float16)
+    hv = hk.copy()
+    sp = np.stack([np.arange(sample), np.arange(sample, 2 * sample)], 1)
+    t = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t < min(args.cpu_seconds, 5.0) or reps == 0:
+        oracle_copy(hk, hv, sp)
+        reps += 1
+    cpu_s = time.perf_counter() - t
+    result = {
+        "metric": f"{args.op} GB/s (K and V blocks moved), 1xMI355X",
+        "value": round(algo * args.steps / (total_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic (normal draws)",
+        "config": {"workload": f"{args.op}: {n} blocks of 32 kv heads x 16 tokens x 128 fp16 (128 KiB of K and "
+                               f"of V each), GPU pools of {NG} blocks, pinned host pools of {NC}",
+                   "pairs": n, "block_bytes": block_bytes},
+        "roofline": {"kernel": "copy_blocks_kernel", "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "GB/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_call_us": round(call_ms * 1e3, 3), "bytes_per_call": algo},
+        "cpu_baseline": {"value": round(2 * 2 * sample * block_bytes * reps / cpu_s / 1e9, 3), "unit": "GB/s",
+                         "cores": 1, "kind": "oracle",
+                         "sample": f"{reps} numpy copies of {sample} block pairs (K and V), one thread"},
+    }
+    print(json.dumps(result), flush=True)
 
 
 def copy_calibration():
@@ -137,6 +232,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.op != "decode":
+        block_moves(args)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

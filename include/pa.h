@@ -60,7 +60,8 @@ typedef enum pa_status {
                                  non-finite scale, partition not a multiple of block_size */
     PA_ERR_UNSUPPORTED = 2,   /* head_dim, block_size, dtype, layout or kernel outside the supported set */
     PA_ERR_WORKSPACE = 3,     /* split-K needs a workspace and the one given is missing or too small */
-    PA_ERR_HIP = 4            /* a HIP launch failed */
+    PA_ERR_HIP = 4,           /* a HIP launch failed */
+    PA_ERR_NO_BLOCKS = 5      /* pa_blocks.h: not enough free blocks; nothing was changed */
 } pa_status;
 
 typedef enum pa_dtype {

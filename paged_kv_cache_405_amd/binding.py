@@ -1,33 +1,36 @@
-"""ctypes binding of libpa_mi355x.so (the C ABI of include/pa.h).
+"""ctypes binding of libpa_mi355x.so (the C ABI of include/pa.h and include/pa_blocks.h).
 
 Argument marshalling only: shapes become ints, tensors become device
 pointers, the current torch stream becomes the hipStream_t.  Every step of
 the computation runs in the library's kernels.  If the library has not been
 built, loading raises ImportError -- there is no fallback path.
 
-The functions carry the C names (pa_decode, pa_decode_ex,
-pa_decode_workspace_bytes, pa_reshape_and_cache, pa_status_string,
-pa_abi_version).  `lib()` returns the raw ctypes handle for callers that
-want to pass pointers themselves.
+The functions carry the C names (pa_decode, pa_decode_ex, pa_decode_path,
+pa_decode_workspace_bytes, pa_reshape_and_cache, pa_copy_blocks,
+pa_swap_blocks, pa_status_string, pa_abi_version); `BlockManager` wraps the
+pa_bm_* calls of the host block manager.  `lib()` returns the raw ctypes
+handle for callers that want to pass pointers themselves.
 """
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
 import re
 import threading
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa_mi355x.so")
-HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pa.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = range(6)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_LAYOUT_BHTD, PA_LAYOUT_BTHD = 0, 1
 PA_KERNEL_AUTO, PA_KERNEL_VECTOR, PA_KERNEL_MFMA = 0, 1, 2
 PA_PARTITION_AUTO, PA_PARTITION_SINGLE, PA_PARTITION_BALANCED = 0, -1, -2
 PA_DECODE_SHARED_BLOCKS = 1
 STATUS_NAMES = {PA_OK: "PA_OK", PA_ERR_INVALID_ARG: "PA_ERR_INVALID_ARG", PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED",
-                PA_ERR_WORKSPACE: "PA_ERR_WORKSPACE", PA_ERR_HIP: "PA_ERR_HIP"}
+                PA_ERR_WORKSPACE: "PA_ERR_WORKSPACE", PA_ERR_HIP: "PA_ERR_HIP", PA_ERR_NO_BLOCKS: "PA_ERR_NO_BLOCKS"}
+POOL_GPU, POOL_CPU = 0, 1
 
 _lock = threading.Lock()
 _lib = None
@@ -39,12 +42,14 @@ class PaError(RuntimeError):
         super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({pa_status_string(status)})")
 
 
-def declared_functions(header: str = HEADER_PATH):
-    """Names of the functions include/pa.h declares."""
-    with open(header) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(", text, flags=re.M)))
+def declared_functions(include_dir: str = INCLUDE_DIR):
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for h in sorted(glob.glob(os.path.join(include_dir, "*.h"))):
+        with open(h) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def lib():
@@ -66,6 +71,37 @@ def lib():
             L.pa_decode_path.argtypes = [i32] * 9 + [ctypes.POINTER(i32), ctypes.POINTER(i32)]
             L.pa_reshape_and_cache.restype = i32
             L.pa_reshape_and_cache.argtypes = [vp] * 5 + [i32] * 7 + [vp]
+            i64, pi32, pi64, vpp = ctypes.c_int64, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_int64), \
+                ctypes.POINTER(vp)
+            L.pa_copy_blocks.restype = i32
+            L.pa_copy_blocks.argtypes = [vp, vp, vp] + [i32] * 6 + [vp]
+            L.pa_swap_blocks.restype = i32
+            L.pa_swap_blocks.argtypes = [vp] * 5 + [i32] * 7 + [vp]
+            L.pa_bm_create.restype = i32
+            L.pa_bm_create.argtypes = [i32, i32, i32, vpp]
+            L.pa_bm_destroy.restype = None
+            L.pa_bm_destroy.argtypes = [vp]
+            L.pa_bm_add.restype = i32
+            L.pa_bm_add.argtypes = [vp, i64]
+            L.pa_bm_fork.restype = i32
+            L.pa_bm_fork.argtypes = [vp, i64, i64]
+            L.pa_bm_blocks_needed.restype = i32
+            L.pa_bm_blocks_needed.argtypes = [vp, i64, i32, pi32]
+            L.pa_bm_append.restype = i32
+            L.pa_bm_append.argtypes = [vp, i64, i32, pi64, pi32, i32, pi32]
+            L.pa_bm_free.restype = i32
+            L.pa_bm_free.argtypes = [vp, i64]
+            for f in (L.pa_bm_swap_out, L.pa_bm_swap_in):
+                f.restype = i32
+                f.argtypes = [vp, i64, pi32, i32, pi32]
+            L.pa_bm_block_tables.restype = i32
+            L.pa_bm_block_tables.argtypes = [vp, pi64, i32, i32, pi32, pi32]
+            L.pa_bm_num_free.restype = i32
+            L.pa_bm_num_free.argtypes = [vp, i32, pi32]
+            L.pa_bm_ref_count.restype = i32
+            L.pa_bm_ref_count.argtypes = [vp, i32, i32, pi32]
+            L.pa_bm_info.restype = i32
+            L.pa_bm_info.argtypes = [vp, i64, pi64, pi32, pi32]
             L.pa_status_string.restype = ctypes.c_char_p
             L.pa_status_string.argtypes = [i32]
             L.pa_abi_version.restype = i32
@@ -230,3 +266,145 @@ def from_layout(cache, layout: int):
     if layout == PA_LAYOUT_BTHD:
         return cache.contiguous()
     return cache.permute(0, 2, 1, 3).contiguous()
+
+
+# ---------------------------------------------------------------------------
+# block copies and the host block manager (include/pa_blocks.h)
+# ---------------------------------------------------------------------------
+def _pool(t, name, dtype):
+    """A pool tensor: device memory, or pinned host memory the device can address."""
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _pairs(pairs):
+    torch = _torch()
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [n, 2]")
+    return _pool(pairs, "pairs", torch.int32), pairs.shape[0]
+
+
+def copy_blocks(k_cache, v_cache, pairs, *, layout=PA_LAYOUT_BHTD, stream=None):
+    """pa_copy_blocks: block pairs[i, 1] of both pools takes block pairs[i, 0]."""
+    NB, bs, Hkv, D = cache_dims(k_cache, layout)
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache differ in shape")
+    ptr, n = _pairs(pairs)
+    st = lib().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype), ptr, n, NB, bs, Hkv,
+                              D, _dtype_code(k_cache), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_copy_blocks")
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, *, layout=PA_LAYOUT_BHTD, stream=None):
+    """pa_swap_blocks: block pairs[i, 1] of the destination pools takes block pairs[i, 0] of the source pools.
+    Either pool pair may be device memory or pinned host memory."""
+    NBd, bs, Hkv, D = cache_dims(dst_k, layout)
+    NBs, bs2, Hkv2, D2 = cache_dims(src_k, layout)
+    if (bs, Hkv, D) != (bs2, Hkv2, D2) or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+        raise ValueError("the pools differ in block shape")
+    dt = dst_k.dtype
+    ptr, n = _pairs(pairs)
+    st = lib().pa_swap_blocks(_pool(dst_k, "dst_k", dt), _pool(dst_v, "dst_v", dt), _pool(src_k, "src_k", dt),
+                              _pool(src_v, "src_v", dt), ptr, n, NBd, NBs, bs, Hkv, D, _dtype_code(dst_k),
+                              _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_swap_blocks")
+
+
+class BlockManager:
+    """The host block manager (pa_bm_*): tables, reference counts and free blocks of a GPU and a CPU pool."""
+
+    def __init__(self, num_gpu_blocks: int, num_cpu_blocks: int, block_size: int):
+        h = ctypes.c_void_p()
+        st = lib().pa_bm_create(num_gpu_blocks, num_cpu_blocks, block_size, ctypes.byref(h))
+        if st != PA_OK:
+            raise PaError(st, "pa_bm_create")
+        self._h = h
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _call(self, name, *args):
+        st = getattr(lib(), name)(self._h, *args)
+        if st != PA_OK:
+            raise PaError(st, name)
+
+    def add(self, seq: int):
+        self._call("pa_bm_add", seq)
+
+    def fork(self, parent: int, child: int):
+        self._call("pa_bm_fork", parent, child)
+
+    def blocks_needed(self, seq: int, n: int) -> int:
+        out = ctypes.c_int32(0)
+        self._call("pa_bm_blocks_needed", seq, n, ctypes.byref(out))
+        return out.value
+
+    def append(self, seq: int, n: int):
+        """(slot of each new token, [(src, dst)] block copies to run first)."""
+        slots = (ctypes.c_int64 * max(n, 1))()
+        copies = (ctypes.c_int32 * 2)()
+        nc = ctypes.c_int32(0)
+        self._call("pa_bm_append", seq, n, slots, copies, 1, ctypes.byref(nc))
+        return list(slots[:n]), [(copies[2 * i], copies[2 * i + 1]) for i in range(nc.value)]
+
+    def free(self, seq: int):
+        self._call("pa_bm_free", seq)
+
+    def _move(self, name, seq):
+        _, nb, _ = self.info(seq)
+        pairs = (ctypes.c_int32 * max(2 * nb, 2))()
+        n = ctypes.c_int32(0)
+        self._call(name, seq, pairs, nb, ctypes.byref(n))
+        return [(pairs[2 * i], pairs[2 * i + 1]) for i in range(n.value)]
+
+    def swap_out(self, seq: int):
+        """[(gpu block, cpu block)] to copy from the GPU pools to the CPU pools."""
+        return self._move("pa_bm_swap_out", seq)
+
+    def swap_in(self, seq: int):
+        """[(cpu block, gpu block)] to copy from the CPU pools to the GPU pools."""
+        return self._move("pa_bm_swap_in", seq)
+
+    def block_tables(self, seqs, max_blocks: int):
+        """(int32 [len(seqs), max_blocks] tables, -1 past the end; int32 [len(seqs)] lengths) as numpy arrays."""
+        import numpy as np
+        n = len(seqs)
+        ids = (ctypes.c_int64 * max(n, 1))(*seqs)
+        tables = np.empty((n, max_blocks), dtype=np.int32)
+        lens = np.empty(n, dtype=np.int32)
+        self._call("pa_bm_block_tables", ids, n, max_blocks,
+                   tables.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                   lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+        return tables, lens
+
+    def num_free(self, pool: int = POOL_GPU) -> int:
+        out = ctypes.c_int32(0)
+        self._call("pa_bm_num_free", pool, ctypes.byref(out))
+        return out.value
+
+    def ref_count(self, pool: int, block: int) -> int:
+        out = ctypes.c_int32(0)
+        self._call("pa_bm_ref_count", pool, block, ctypes.byref(out))
+        return out.value
+
+    def info(self, seq: int):
+        """(tokens, blocks, on the GPU)."""
+        t, b, g = ctypes.c_int64(0), ctypes.c_int32(0), ctypes.c_int32(0)
+        self._call("pa_bm_info", seq, ctypes.byref(t), ctypes.byref(b), ctypes.byref(g))
+        return t.value, b.value, bool(g.value)

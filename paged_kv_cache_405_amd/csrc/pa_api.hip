@@ -12,6 +12,7 @@
 #include <tuple>
 
 #include "pa.h"
+#include "pa_blocks.h"
 #include "pa_internal.h"
 
 namespace {
@@ -395,6 +396,80 @@ pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void
     return pa::launch_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+static pa_status copy_blocks_common(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
+                                    const int32_t *pairs, int num_pairs, int num_dst_blocks, int num_src_blocks,
+                                    int block_size, int num_kv_heads, int head_dim, pa_dtype dtype, void *stream)
+{
+    if (num_pairs < 0 || num_dst_blocks <= 0 || num_src_blocks <= 0 || num_kv_heads <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (num_pairs == 0)
+        return PA_OK;
+    if (!dst_k || !dst_v || !src_k || !src_v || !pairs)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(dst_k, 16) || !aligned(dst_v, 16) || !aligned(src_k, 16) || !aligned(src_v, 16) ||
+        !aligned(pairs, 4))
+        return PA_ERR_INVALID_ARG;
+    pa::CopyParams c;
+    c.dst_k = dst_k;
+    c.dst_v = dst_v;
+    c.src_k = src_k;
+    c.src_v = src_v;
+    c.pairs = pairs;
+    c.num_pairs = num_pairs;
+    c.num_src_blocks = num_src_blocks;
+    c.num_dst_blocks = num_dst_blocks;
+    c.block_bytes = (int64_t)block_size * num_kv_heads * head_dim * elem_bytes(dtype);
+    return pa::launch_copy_blocks(c, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int num_pairs, int num_blocks,
+                         int block_size, int num_kv_heads, int head_dim, pa_dtype dtype, void *stream)
+{
+    return copy_blocks_common(k_cache, v_cache, k_cache, v_cache, pairs, num_pairs, num_blocks, num_blocks,
+                              block_size, num_kv_heads, head_dim, dtype, stream);
+}
+
+// The address a kernel uses for p: p itself for device (or managed) memory,
+// the device mapping of pinned host memory.  False for memory the device
+// cannot reach (pageable host memory), which must never get to a kernel.
+static bool device_address(const void *p, const void **out)
+{
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+        *out = p;
+        return true;
+    }
+    if (a.type == hipMemoryTypeHost && a.devicePointer) {
+        const ptrdiff_t off = a.hostPointer ? static_cast<const char *>(p) - static_cast<const char *>(a.hostPointer) : 0;
+        *out = static_cast<const char *>(a.devicePointer) + off;
+        return true;
+    }
+    return false;
+}
+
+pa_status pa_swap_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v, const int32_t *pairs,
+                         int num_pairs, int num_dst_blocks, int num_src_blocks, int block_size, int num_kv_heads,
+                         int head_dim, pa_dtype dtype, void *stream)
+{
+    if (num_pairs > 0 && dst_k && dst_v && src_k && src_v && pairs) {
+        const void *dk, *dv, *sk, *sv, *pp;
+        if (!device_address(dst_k, &dk) || !device_address(dst_v, &dv) || !device_address(src_k, &sk) ||
+            !device_address(src_v, &sv) || !device_address(pairs, &pp))
+            return PA_ERR_INVALID_ARG;
+        return copy_blocks_common(const_cast<void *>(dk), const_cast<void *>(dv), sk, sv,
+                                  static_cast<const int32_t *>(pp), num_pairs, num_dst_blocks, num_src_blocks,
+                                  block_size, num_kv_heads, head_dim, dtype, stream);
+    }
+    return copy_blocks_common(dst_k, dst_v, src_k, src_v, pairs, num_pairs, num_dst_blocks, num_src_blocks,
+                              block_size, num_kv_heads, head_dim, dtype, stream);
+}
+
 const char *pa_status_string(pa_status status)
 {
     switch (status) {
@@ -403,6 +478,7 @@ const char *pa_status_string(pa_status status)
     case PA_ERR_UNSUPPORTED: return "unsupported shape, element type or layout";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP launch failed";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks";
     default: return "unknown status";
     }
 }

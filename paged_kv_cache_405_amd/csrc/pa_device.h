@@ -341,4 +341,16 @@ struct AppendParams {
     int elem_bytes;
 };
 
+// whole-block copies (pa_copy_blocks, pa_swap_blocks)
+struct CopyParams {
+    void *dst_k;
+    void *dst_v;
+    const void *src_k;
+    const void *src_v;
+    const int32_t *pairs;     // [num_pairs][2] (source block, destination block)
+    int num_pairs;
+    int num_src_blocks, num_dst_blocks;
+    int64_t block_bytes;      // a multiple of 16
+};
+
 }  // namespace pa

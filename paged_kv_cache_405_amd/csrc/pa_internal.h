@@ -1,4 +1,4 @@
-// pa_internal.h -- launchers shared between the C ABI (pa_api.cpp) and the
+// pa_internal.h -- launchers shared between the C ABI (pa_api.hip) and the
 // kernel translation units.  Not part of the public interface.
 #pragma once
 
@@ -32,5 +32,6 @@ hipError_t stream_mfma_bf16(const DecodeParams *p, int head_dim, int block_size,
 // merge the pieces the stream kernel left (one workgroup per unit)
 hipError_t launch_stream_reduce(const DecodeParams &p, int dtype, int head_dim, int heads_per_unit, hipStream_t st);
 hipError_t launch_append(const AppendParams &p, hipStream_t st);
+hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t st);
 
 }  // namespace pa

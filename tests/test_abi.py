@@ -205,3 +205,29 @@ def test_decode_path_resolves_explicit_choices_without_a_device():
 def test_decode_rejects_unknown_flags(flags):
     # checked before anything else, so no device is needed to see it
     assert _decode(flags=flags) == B.PA_ERR_INVALID_ARG
+
+
+def test_block_copies_check_arguments_first(L):
+    # argument and shape errors come back before any device use; zero pairs is a no-op
+    args = lambda **kw: dict(dict(k=FAKE, v=FAKE, pairs=FAKE, n=3, NB=8, bs=16, Hkv=2, D=64, dt=B.PA_F16), **kw)  # noqa
+    def copy(**kw):
+        a = args(**kw)
+        return L.pa_copy_blocks(a["k"], a["v"], a["pairs"], a["n"], a["NB"], a["bs"], a["Hkv"], a["D"], a["dt"], None)
+    assert copy(n=0) == B.PA_OK
+    assert copy(n=-1) == B.PA_ERR_INVALID_ARG
+    assert copy(k=None) == B.PA_ERR_INVALID_ARG
+    assert copy(k=FAKE + 8) == B.PA_ERR_INVALID_ARG
+    assert copy(pairs=FAKE + 2) == B.PA_ERR_INVALID_ARG
+    assert copy(NB=0) == B.PA_ERR_INVALID_ARG
+    assert copy(D=48) == B.PA_ERR_UNSUPPORTED
+    assert copy(bs=64) == B.PA_ERR_UNSUPPORTED
+    assert copy(dt=7) == B.PA_ERR_UNSUPPORTED
+    swap = lambda n: L.pa_swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, n, 8, 8, 16, 2, 64, B.PA_F16, None)  # noqa
+    assert swap(0) == B.PA_OK
+    assert L.pa_swap_blocks(None, FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 16, 2, 64, B.PA_F16, None) == B.PA_ERR_INVALID_ARG
+
+
+@host_only
+def test_swap_looks_up_every_pointer(L):
+    # with no device, no pointer can be shown to be device-addressable: refused before any launch
+    assert L.pa_swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 16, 2, 64, B.PA_F16, None) == B.PA_ERR_INVALID_ARG
