@@ -205,6 +205,36 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
                        unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pa_prefill -- paged attention for several query rows per sequence: a
+ * prefill chunk, or drafted tokens to verify ("vLLM 与 PagedAttention"
+ * section 六, "关键的工程优化": a long prompt's prefill in chunks next to
+ * decode; "指南", "Speculative Decoding" and "Chunked Prefill").  The chunk's
+ * own K/V rows are appended first (pa_reshape_and_cache); then query row i of
+ * a sequence with n rows and context_lens L sits at position L - n + i and
+ * attends tokens 0 .. L - n + i of its history (causal).  A row with no token
+ * to attend (n > L) is zero.
+ *
+ *   out, q          [total_q, num_q_heads, head_dim] dtype: the rows of all
+ *                   sequences, back to back
+ *   query_start     int32 [num_seqs + 1], device: the rows of sequence s are
+ *                   q[query_start[s] .. query_start[s + 1]); query_start[0] = 0,
+ *                   query_start[num_seqs] = total_q; rows outside
+ *                   [0, total_q) are never read or written
+ *   max_query_len   the most rows of any sequence (sizes the grid; rows past
+ *                   it are not computed)
+ *   other arguments as for pa_decode_ex; flags: 0 or PA_DECODE_SHARED_BLOCKS
+ *
+ * Runs on the matrix cores: f16 or bf16, head_dim 128 or 256, at most 16 q
+ * heads per kv head or a multiple of 16; otherwise PA_ERR_UNSUPPORTED.  No
+ * workspace.  Errors as for pa_decode_ex.
+ */
+pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, const int32_t *context_lens, const int32_t *query_start,
+                     int num_seqs, int total_q, int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int block_size, int max_blocks_per_seq, int num_blocks, float scale, pa_dtype dtype,
+                     pa_layout layout, unsigned flags, void *stream);
+
+/*
  * pa_decode_path -- the path pa_decode_ex takes for these sizes, with the
  * automatic choices resolved: *partition_out receives PA_PARTITION_SINGLE,
  * PA_PARTITION_BALANCED or the partition in tokens, *kernel_out

@@ -102,6 +102,8 @@ def lib():
             L.pa_bm_ref_count.argtypes = [vp, i32, i32, pi32]
             L.pa_bm_info.restype = i32
             L.pa_bm_info.argtypes = [vp, i64, pi64, pi32, pi32]
+            L.pa_prefill.restype = i32
+            L.pa_prefill.argtypes = [vp] * 7 + [i32] * 9 + [f32, i32, i32, ctypes.c_uint32, vp]
             L.pa_status_string.restype = ctypes.c_char_p
             L.pa_status_string.argtypes = [i32]
             L.pa_abi_version.restype = i32
@@ -214,6 +216,29 @@ def pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, *,
         None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode_ex")
+    return out
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, scale, *,
+               num_blocks=None, layout=PA_LAYOUT_BHTD, shared_blocks=False, stream=None):
+    """out[total_q, Hq, D] <- causal paged attention of the q rows of every sequence (query_start [S + 1])."""
+    torch = _torch()
+    code = _dtype_code(q)
+    TQ, Hq, D = q.shape
+    NB, bs, Hkv, D2 = cache_dims(k_cache, layout)
+    S = context_lens.shape[0]
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, out and the caches")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(query_start.shape) != (S + 1,):
+        raise ValueError("block_tables must be [S, MB] and query_start [S + 1]")
+    st = lib().pa_prefill(
+        _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        _dev(query_start, "query_start", torch.int32), S, TQ, int(max_query_len), Hq, Hkv, D, bs,
+        block_tables.shape[1], NB if num_blocks is None else int(num_blocks), float(scale), code, int(layout),
+        PA_DECODE_SHARED_BLOCKS if shared_blocks else 0, _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_prefill")
     return out
 
 

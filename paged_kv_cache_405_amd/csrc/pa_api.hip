@@ -396,6 +396,61 @@ pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void
     return pa::launch_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, const int32_t *context_lens, const int32_t *query_start,
+                     int num_seqs, int total_q, int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int block_size, int max_blocks_per_seq, int num_blocks, float scale, pa_dtype dtype,
+                     pa_layout layout, unsigned flags, void *stream)
+{
+    if (flags & ~(unsigned)PA_DECODE_SHARED_BLOCKS)
+        return PA_ERR_INVALID_ARG;
+    pa_status st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                               dtype, PA_PARTITION_SINGLE);
+    if (st != PA_OK)
+        return st;
+    const int group = num_q_heads / num_kv_heads;
+    if (!mfma_shape(dtype, head_dim, group) || !supported_layout(layout))
+        return PA_ERR_UNSUPPORTED;
+    if (total_q < 0 || max_query_len < 0 || num_blocks <= 0 || !std::isfinite(scale))
+        return PA_ERR_INVALID_ARG;
+    if (num_seqs > 65535 || (long long)num_kv_heads * (group <= 16 ? 1 : group / 16) > 65535)
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || total_q == 0 || max_query_len == 0)
+        return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+        return PA_ERR_INVALID_ARG;
+
+    pa::DecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.out = out;
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.tables = block_tables;
+    p.ctx = context_lens;
+    p.query_start = query_start;
+    p.total_q = total_q;
+    p.kv_cached = (flags & PA_DECODE_SHARED_BLOCKS) ? 1 : 0;
+    layout_strides(layout, num_kv_heads, block_size, head_dim, &p.block_stride, &p.head_stride, &p.token_stride);
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.partition_blocks = max_blocks_per_seq;
+    p.max_partitions = 1;
+    p.group = group;
+    p.group_split = group <= 16 ? 1 : group / 16;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == PA_F16 ? pa::launch_prefill_f16(p, head_dim, block_size, max_query_len, s)
+                                         : pa::launch_prefill_bf16(p, head_dim, block_size, max_query_len, s);
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 static pa_status copy_blocks_common(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
                                     const int32_t *pairs, int num_pairs, int num_dst_blocks, int num_src_blocks,
                                     int block_size, int num_kv_heads, int head_dim, pa_dtype dtype, void *stream)

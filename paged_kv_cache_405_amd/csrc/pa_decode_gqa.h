@@ -269,7 +269,13 @@ struct GqaWorker {
     const int32_t __attribute__((address_space(4))) *trow;   // constant space: read-only during the kernel, always scalar loads
     int64_t blk_bytes, tok_bytes;
     int nblk, num_blocks;
-    int t_lo, t_hi;
+    // token limits of the unit: a token t enters the scores of this lane's
+    // column when t_lo <= t < t_hi (t_hi differs per column when columns are
+    // query rows at different positions); its V rows are read only when
+    // t < t_vlim (the tokens inside the context); tiles below t_full are
+    // valid for every column (the unmasked path)
+    int t_lo, t_hi, t_vlim, t_full;
+    int ncols;                // score columns that carry an output row
     float scale_log2;
     int lr, lg;
     int k_lane;               // byte offset of this lane's K row / dims inside a tile
@@ -289,23 +295,12 @@ struct GqaWorker {
     __device__ __forceinline__ void init_lds(unsigned char PA_LDS *base) { lds = base; }
     __device__ __forceinline__ void bind_buf(Buf &b, int slot) const { b.v = lds + slot * TILE_LDS; }
 
-    __device__ __forceinline__ void bind(const DecodeParams &P, int s, int hg, int ctx) {
+    // the parts of a unit that do not depend on what the columns are
+    __device__ __forceinline__ void bind_kv(const DecodeParams &P, int s, int hg, int ctx) {
         const int kvh = hg / P.group_split;
         seq = s;
         gh = P.group / P.group_split;
-        dup = gh <= 8;
-        lo_lane = dup && lr >= 8;
         qh0 = kvh * P.group + (hg - kvh * P.group_split) * gh;
-        const int hq = dup ? (lr & 7) : lr;          // head of this lane's column
-        const bool on = hq < gh;
-        const char *qp = static_cast<const char *>(P.q) +
-                         (((int64_t)s * P.num_q_heads + qh0 + (on ? hq : 0)) * D + 8 * lg) * ES;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            qb[c] = ld16(qp + 32 * c * ES);
-            if (!on)
-                qb[c] = make_uint4(0u, 0u, 0u, 0u);
-        }
         blk_bytes = P.block_stride * ES;
         tok_bytes = P.token_stride * ES;
         kpool = static_cast<const char *>(P.k) + (int64_t)kvh * P.head_stride * ES;
@@ -314,8 +309,6 @@ struct GqaWorker {
         nblk = (ctx + BS - 1) / BS;
         num_blocks = P.num_blocks;
         scale_log2 = P.scale_log2;
-        t_lo = 0;
-        t_hi = ctx;
         constexpr int RW = BS < GQA_TILE ? BS : GQA_TILE;
         k_lane = (int)((lr % RW) * tok_bytes) + 8 * lg * ES;
         // direct load i, lane l: token 4i + l % 4 (of the tile), 16-byte chunk l / 4 (plus 16 per
@@ -327,6 +320,55 @@ struct GqaWorker {
         tr_off = lg * (D / 128) * LOAD_LDS + (lr / 4) * 16 + ((lr % 4) / 2) * 64 + (lr % 2) * 8;
     }
 
+    __device__ __forceinline__ void load_q(const char *qp, bool on) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            qb[c] = ld16(qp + 32 * c * ES);
+            if (!on)
+                qb[c] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+
+    // decode: the columns are the unit's gh q heads (entered twice when gh <= 8)
+    __device__ __forceinline__ void bind(const DecodeParams &P, int s, int hg, int ctx) {
+        bind_kv(P, s, hg, ctx);
+        dup = gh <= 8;
+        lo_lane = dup && lr >= 8;
+        ncols = gh;
+        const int hq = dup ? (lr & 7) : lr;          // head of this lane's column
+        const bool on = hq < gh;
+        load_q(static_cast<const char *>(P.q) + (((int64_t)s * P.num_q_heads + qh0 + (on ? hq : 0)) * D + 8 * lg) * ES,
+               on);
+        t_lo = 0;
+        t_hi = t_vlim = t_full = ctx;
+    }
+
+    // several query rows: column c is query row i0 + c / gh (at position
+    // ctx - nq + that row), head c % gh, for the 16 / gh rows of the tile;
+    // row q_first of q is query row 0 of the sequence.  Columns past the
+    // tile's rows read nothing and write nothing; they follow the first row's
+    // limit so that they never force the masked path.
+    __device__ __forceinline__ void bind_rows(const DecodeParams &P, int s, int hg, int ctx, int q_first, int nq,
+                                              int i0) {
+        bind_kv(P, s, hg, ctx);
+        dup = false;
+        lo_lane = false;
+        const int rows = GQA_TILE / gh;
+        ncols = rows * gh;
+        const int i = i0 + lr / gh;
+        const bool on = lr < ncols && i < nq;
+        load_q(static_cast<const char *>(P.q) +
+                   (((int64_t)(q_first + (on ? i : i0))) * P.num_q_heads + qh0 + (on ? lr % gh : 0)) * D * ES +
+                   8 * lg * ES,
+               on);
+        auto limit = [&](int row) { const int t = ctx - nq + row + 1; return t < 0 ? 0 : (t > ctx ? ctx : t); };
+        t_lo = 0;
+        t_vlim = ctx;
+        t_full = limit(i0);
+        t_hi = on ? limit(i) : t_full;
+        t_last = limit(min(i0 + rows, nq) - 1);
+    }
+    int t_last;               // bind_rows: one past the last token any column attends
     __device__ __forceinline__ void reset() {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -409,7 +451,7 @@ struct GqaWorker {
             sc = Ops::score(make_uint4(b.k[c].x, b.k[c].y, b.k[c].z, b.k[c].w), qb[c], sc);
         const int t0 = kt * GQA_TILE;
         const int tv = t0 + 4 * lg;                   // this lane's four tokens tv + r
-        const bool full = b.oka && b.okb && t0 >= t_lo && t0 + GQA_TILE <= t_hi;
+        const bool full = b.oka && b.okb && t0 >= t_lo && t0 + GQA_TILE <= t_full;
         const bool okv = (BS < GQA_TILE && 4 * lg >= BS) ? b.okb : b.oka;
         float sv[4];
         uint32_t keep[2] = {0xffffffffu, 0xffffffffu};   // 16-bit lanes of the V fragment to keep
@@ -417,14 +459,15 @@ struct GqaWorker {
         for (int r = 0; r < 4; ++r)
             sv[r] = sc[r] * scale_log2;
         if (!full) {
-            bool valid[4];
+            bool valid[4], readable[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                valid[r] = okv && tv + r >= t_lo && tv + r < t_hi;
+                readable[r] = okv && tv + r >= t_lo && tv + r < t_vlim;   // its V rows may be used
+                valid[r] = readable[r] && tv + r < t_hi;                 // it enters this column's scores
                 sv[r] = valid[r] ? sv[r] : -INFINITY;
             }
-            keep[0] = (valid[0] ? 0x0000ffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
-            keep[1] = (valid[2] ? 0x0000ffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
+            keep[0] = (readable[0] ? 0x0000ffffu : 0u) | (readable[1] ? 0xffff0000u : 0u);
+            keep[1] = (readable[2] ? 0x0000ffffu : 0u) | (readable[3] ? 0xffff0000u : 0u);
         }
         const float mx = max_token_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
         // lazy rescale: move the reference max only when this tile's max exceeds it by 2^8
@@ -516,7 +559,7 @@ struct GqaWorker {
         }
     }
     __device__ __forceinline__ bool owns(int r) const {
-        return (!dup || lg < 2) && 4 * lg + r < gh;
+        return (!dup || lg < 2) && 4 * lg + r < ncols;
     }
     __device__ __forceinline__ int row_head(int r) const { return 4 * lg + r; }
 

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     const int b0 = p * P.partition_blocks;
     const int b1 = min(nblk, b0 + P.partition_blocks);
     w.t_lo = b0 * BS;
-    w.t_hi = min(b1 * BS, ctx);
+    w.t_hi = w.t_vlim = w.t_full = min(b1 * BS, ctx);
     const int k0 = w.t_lo / GQA_TILE;
     const int k1 = (w.t_hi + GQA_TILE - 1) / GQA_TILE;
     w.reset();

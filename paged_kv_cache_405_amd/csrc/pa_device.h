@@ -319,6 +319,8 @@ struct DecodeParams {
     // all (head group, sequence) units; a unit cut between waves leaves pieces
     int n_waves;              // logical waves of the stream kernel (a multiple of 8)
     int kv_cached;            // 1: blocks may be shared across sequences -- plain (cached) K/V loads
+    const int32_t *query_start;   // multi-token calls: [num_seqs + 1] first q row of each sequence
+    int total_q;                  // multi-token calls: rows of q and out
     uint64_t *stream_total;   // [1] steps of the whole stream (T), written by the stream kernel
     int32_t *unit_first;      // [HG * S] first piece of each unit, -1 when one wave finished it
     int32_t *unit_last;       // [HG * S] last piece of each cut unit

@@ -33,5 +33,8 @@ hipError_t stream_mfma_bf16(const DecodeParams *p, int head_dim, int block_size,
 hipError_t launch_stream_reduce(const DecodeParams &p, int dtype, int head_dim, int heads_per_unit, hipStream_t st);
 hipError_t launch_append(const AppendParams &p, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t st);
+// multi-token paged attention on the matrix cores (f16 / bf16, head_dim 128 or 256)
+hipError_t launch_prefill_f16(const DecodeParams &p, int head_dim, int block_size, int max_query_len, hipStream_t st);
+hipError_t launch_prefill_bf16(const DecodeParams &p, int head_dim, int block_size, int max_query_len, hipStream_t st);
 
 }  // namespace pa

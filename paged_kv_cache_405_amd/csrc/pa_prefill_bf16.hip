@@ -1,0 +1,12 @@
+// pa_prefill_bf16.hip -- multi-token paged attention instances for bf16.
+#include "pa_internal.h"
+#include "pa_prefill.h"
+
+namespace pa {
+
+hipError_t launch_prefill_bf16(const DecodeParams &p, int head_dim, int block_size, int max_query_len, hipStream_t st)
+{
+    return launch_prefill_dtype<bf16_t>(p, head_dim, block_size, max_query_len, st);
+}
+
+}  // namespace pa

@@ -231,3 +231,26 @@ def test_block_copies_check_arguments_first(L):
 def test_swap_looks_up_every_pointer(L):
     # with no device, no pointer can be shown to be device-addressable: refused before any launch
     assert L.pa_swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 16, 2, 64, B.PA_F16, None) == B.PA_ERR_INVALID_ARG
+
+
+def _prefill(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, S=2, TQ=10, MQ=8, Hq=8, Hkv=2, D=128,
+             bs=16, MB=8, NB=32, scale=0.125, dt=B.PA_F16, layout=B.PA_LAYOUT_BHTD, flags=0)
+    a.update(kw)
+    return B.lib().pa_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["S"], a["TQ"], a["MQ"],
+                              a["Hq"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["scale"], a["dt"], a["layout"],
+                              a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=0), B.PA_OK), (dict(TQ=0), B.PA_OK), (dict(MQ=0), B.PA_OK),
+    (dict(flags=2), B.PA_ERR_INVALID_ARG),
+    (dict(TQ=-1), B.PA_ERR_INVALID_ARG), (dict(MQ=-1), B.PA_ERR_INVALID_ARG),
+    (dict(qs=None), B.PA_ERR_INVALID_ARG), (dict(qs=FAKE + 2), B.PA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), B.PA_ERR_INVALID_ARG), (dict(NB=0), B.PA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), B.PA_ERR_INVALID_ARG), (dict(Hq=6, Hkv=4), B.PA_ERR_INVALID_ARG),
+    (dict(dt=B.PA_F32), B.PA_ERR_UNSUPPORTED), (dict(D=64), B.PA_ERR_UNSUPPORTED),
+    (dict(Hq=40, Hkv=2), B.PA_ERR_UNSUPPORTED), (dict(layout=5), B.PA_ERR_UNSUPPORTED),
+])
+def test_prefill_checks_arguments_first(kw, status):
+    assert _prefill(**kw) == status

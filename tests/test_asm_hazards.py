@@ -79,7 +79,7 @@ def test_checker_accepts_covered_use():
     assert asm_hazards.check_assembly(CLEAN)["_Z6kernelv"] == []
 
 
-MFMA_SOURCES = [s for s in B.sources() if "mfma" in os.path.basename(s)]
+MFMA_SOURCES = [s for s in B.sources() if "mfma" in os.path.basename(s) or "prefill" in os.path.basename(s)]
 
 
 @pytest.mark.skipif(not os.path.exists(B.HIPCC), reason="hipcc not installed")
