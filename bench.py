@@ -50,9 +50,10 @@ def parse(argv=None):
                     help="decode kernel family (pa_kernel): auto picks matrix cores for grouped-query heads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["decode", "copy_blocks", "swap_out", "swap_in"], default="decode",
-                    help="decode (the default step) or one of the block moves of the paging system: copy_blocks "
-                         "(copy on write inside the GPU pools), swap_out / swap_in (GPU pools <-> pinned host pools)")
+    ap.add_argument("--op", choices=["decode", "prefill", "copy_blocks", "swap_out", "swap_in"], default="decode",
+                    help="decode (the default step); prefill (a 512-token chunk per sequence over a 1536-token "
+                         "cached history); or one of the block moves of the paging system: copy_blocks (copy on "
+                         "write inside the GPU pools), swap_out / swap_in (GPU pools <-> pinned host pools)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device a few times (the known-size kernel that scales the "
                          "HBM byte counters of a profiler run) and exit")
@@ -60,6 +61,96 @@ def parse(argv=None):
 
 
 HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense f16 / bf16 matrix-core peak of the MI355X
+
+
+def prefill_step(args):
+    """Time chunked prefill (pa_prefill) on Llama-2-7B-shaped layers: 16 sequences, each appending and
+    attending a 512-token chunk over a 1536-token cached history (context 2048), 32 x 128 MHA heads, fp16,
+    block size 16; 8 layers with their own pools."""
+    import torch
+    from paged_kv_cache_405_amd import binding as B
+    from oracle.prefill import paged_prefill
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+    S, chunk, hist, H, D, bs = 16, 512, 1536, 32, 128, 16
+    ctx = hist + chunk
+    layers = args.layers or 8
+    nblk = ctx // bs
+    NB = S * nblk + S * nblk // 10
+    rng = np.random.default_rng(21)
+    # distinct blocks for every sequence: one permutation of the pool
+    perm = rng.permutation(NB)
+    tables = perm[:S * nblk].reshape(S, nblk).astype(np.int32)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(22)
+    Ls = []
+    for _ in range(layers):
+        kc = torch.randn((NB, H, bs, D), generator=gen, device=dev, dtype=torch.float16)
+        vc = torch.randn_like(kc)
+        q = torch.randn((S * chunk, H, D), generator=gen, device=dev, dtype=torch.float16)
+        Ls.append((kc, vc, q, torch.empty_like(q)))
+    t_dev = torch.from_numpy(tables).to(dev)
+    ctx_dev = torch.full((S,), ctx, dtype=torch.int32, device=dev)
+    qs_dev = torch.arange(0, S * chunk + 1, chunk, dtype=torch.int32, device=dev)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for li, (kc, vc, q, out) in enumerate(Ls):
+            if events is not None:
+                events[li][0].record(stream)
+            B.pa_prefill(out, q, kc, vc, t_dev, ctx_dev, qs_dev, chunk, scale, stream=stream)
+            if events is not None:
+                events[li][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
+           for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    call_ms = statistics.fmean(a.elapsed_time(b) for e in evs for a, b in e)
+    # algorithmic work: query row i of a chunk attends hist + i + 1 tokens; 2 D flops for q.k and 2 D for p.v
+    attended = S * sum(hist + i + 1 for i in range(chunk))
+    flops = attended * H * 4 * D
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    calls = args.steps * layers
+    # the oracle, as it is, on one sequence of the same shape (K/V drawn on the host)
+    hk = fp16_storage(rng.standard_normal((nblk, bs, H, D), dtype=np.float32))
+    hv = fp16_storage(rng.standard_normal((nblk, bs, H, D), dtype=np.float32))
+    hq = fp16_storage(rng.standard_normal((chunk, H, D), dtype=np.float32))
+    t = time.perf_counter()
+    paged_prefill(hq, hk, hv, np.arange(nblk, dtype=np.int32)[None], np.array([ctx], np.int32),
+                  np.array([0, chunk], np.int32), scale, "f16")
+    cpu_s = time.perf_counter() - t
+    result = {
+        "metric": "paged prefill TFLOP/s (causal chunk over a paged history), 1xMI355X",
+        "value": round(flops * calls / (total_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic (normal draws)",
+        "config": {"workload": f"prefill: {S} seqs x {chunk}-token chunk over {hist} cached tokens, {H}x{D} MHA, "
+                               f"fp16, bs {bs}, {layers} layers", "chunk": chunk, "history": hist},
+        "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_call_us": round(call_ms * 1e3, 3), "flops_per_call": flops},
+        "cpu_baseline": {"value": round(flops / S / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                         "sample": f"one sequence of the same shape ({chunk} rows over {ctx} tokens), fp64 numpy"},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def fp16_storage(x32):
+    """fp32 draws rounded to fp16 storage."""
+    return x32.astype(np.float16)
 
 
 def block_moves(args):
@@ -232,6 +323,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.op == "prefill":
+        prefill_step(args)
         return
     if args.op != "decode":
         block_moves(args)
