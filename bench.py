@@ -97,27 +97,22 @@ def prefill_step(args):
     scale = float(np.float32(1 / np.sqrt(D)))
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
-        for li, (kc, vc, q, out) in enumerate(Ls):
-            if events is not None:
-                events[li][0].record(stream)
+    def step():
+        for kc, vc, q, out in Ls:
             B.pa_prefill(out, q, kc, vc, t_dev, ctx_dev, qs_dev, chunk, scale, stream=stream)
-            if events is not None:
-                events[li][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
-           for _ in range(args.steps)]
+    # the calls back to back between one pair of events
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for k in range(args.steps):
-        step(evs[k])
+        step()
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    call_ms = statistics.fmean(a.elapsed_time(b) for e in evs for a, b in e)
+    call_ms = total_ms / (args.steps * layers)
     # algorithmic work: query row i of a chunk attends hist + i + 1 tokens; 2 D flops for q.k and 2 D for p.v
     attended = S * sum(hist + i + 1 for i in range(chunk))
     flops = attended * H * 4 * D
@@ -194,17 +189,15 @@ def block_moves(args):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # the calls back to back between one pair of events
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for a, b in evs:
-        a.record(stream)
+    for _ in range(args.steps):
         call()
-        b.record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    call_ms = statistics.fmean(a.elapsed_time(b) for a, b in evs)
+    call_ms = total_ms / args.steps
     moved = 2 * n * block_bytes                      # K and V blocks
     if args.op == "copy_blocks":
         bound, peak, algo = "hbm", HBM_PEAK_GBS, 2 * moved     # read and write, both in HBM
@@ -418,7 +411,22 @@ def main():
     call_ms = [ev[k][2 * li].elapsed_time(ev[k][2 * li + 1]) for k in range(args.steps) for li in range(layers)]
     avg_call_ms = statistics.fmean(call_ms)
     log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms (wall {wall * 1e3:.3f} ms); "
-        f"decode call avg {avg_call_ms * 1e3:.2f} us, median {statistics.median(call_ms) * 1e3:.2f} us")
+        f"decode call between its own events avg {avg_call_ms * 1e3:.2f} us, "
+        f"median {statistics.median(call_ms) * 1e3:.2f} us")
+    # the launch duration of a decode call: the same calls back to back, one
+    # event pair around all of them (an event pair per call adds its own
+    # few microseconds to every call it brackets)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for k in range(args.steps):
+        for kc, vc, q, nk, nv, out in Ls:
+            B.pa_decode_ex(out, q, kc, vc, tables, ctx, w.scale, layout=layout, partition_tokens=pt,
+                           kernel=kern, shared_blocks=shared, workspace=ws, stream=stream)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    evented_call_ms = avg_call_ms
+    avg_call_ms = d0.elapsed_time(d1) / (args.steps * layers)
+    log(f"[bench] decode calls back to back: {avg_call_ms * 1e3:.2f} us per call")
 
     # HBM bytes per call from the committed counter record, when it was taken
     # on these kernel sources (else null)
@@ -465,6 +473,7 @@ def main():
             "traffic": traffic_bytes,
             "traffic_source": traffic_source,
             "avg_call_us": round(avg_call_ms * 1e3, 3),
+            "avg_call_us_own_events": round(evented_call_ms * 1e3, 3),
             "bytes_per_call": kv_per_layer,
         },
         "append_and_decode_us_per_layer": round(total_ms * 1e3 / calls, 3),

@@ -155,7 +155,7 @@ pa_status make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_di
         if (occ <= 0)
             return PA_ERR_HIP;
         long long waves = (long long)cus * occ / 8 * 8;
-        waves = waves < 8 ? 8 : (waves > (1 << 20) ? (1 << 20) : waves);
+        waves = waves < 8 ? 8 : (waves > (1 << 16) ? (1 << 16) : waves);   // N <= 2^16: 32-bit range arithmetic
         pl->stream = true;
         pl->n_waves = (int)waves;
         pl->partition_blocks = max_blocks_per_seq;

@@ -58,8 +58,14 @@ __device__ __forceinline__ int64_t wave_incl_scan64(int64_t x, int lane) {
     return x;
 }
 
-// first stream position of logical wave w: floor(w * T / N) without overflow
+// first stream position of logical wave w: floor(w * T / N) without
+// overflow.  With T < 2^32 and N <= 2^16 (the host keeps N there) every
+// division is a 32-bit one: r * w < N^2 <= 2^32.
 __device__ __forceinline__ uint64_t range_start(int w, uint64_t T, int N) {
+    if (T < (1ull << 32)) {
+        const uint32_t t = (uint32_t)T, n = (uint32_t)N, q = t / n, r = t - q * n;
+        return (uint64_t)q * (uint32_t)w + (uint64_t)((r * (uint32_t)w) / n);
+    }
     const uint64_t q = T / (uint64_t)N, r = T % (uint64_t)N;
     return q * (uint64_t)w + (r * (uint64_t)w) / (uint64_t)N;
 }
@@ -87,12 +93,25 @@ void decode_stream_kernel(const DecodeParams P)
     const int cap = P.max_blocks * BS;
     auto clamp_ctx = [&](int c) { return c < 0 ? 0 : (c > cap ? cap : c); };
 
-    // steps per head group: Tseq = sum over sequences of n(s)
+    // steps per head group: Tseq = sum over sequences of n(s).  Up to 64
+    // sequences (one per lane) the context lengths are read once and kept:
+    // the running sum that gives Tseq also locates the wave's first unit
+    constexpr bool SEQ_MAJOR = PA_STREAM_SEQ_MAJOR != 0;
+    const bool few = !SEQ_MAJOR && S <= 64;
+    int ctx_lane = 0;              // few: lane i holds sequence i's clamped context
+    int64_t incl_lane = 0, n_lane = 0;
     int64_t tseq = 0;
-    for (int b = 0; b < S; b += 64) {
-        const int i = b + lane;
-        const int64_t n = i < S ? max(1, (clamp_ctx(P.ctx[i]) + STEP - 1) / STEP) : 0;
-        tseq += wave_sum64(n);
+    if (few) {
+        ctx_lane = lane < S ? clamp_ctx(P.ctx[lane]) : 0;
+        n_lane = lane < S ? max(1, (ctx_lane + STEP - 1) / STEP) : 0;
+        incl_lane = wave_incl_scan64(n_lane, lane);
+        tseq = uniform64(__shfl(incl_lane, 63));
+    } else {
+        for (int b = 0; b < S; b += 64) {
+            const int i = b + lane;
+            const int64_t n = i < S ? max(1, (clamp_ctx(P.ctx[i]) + STEP - 1) / STEP) : 0;
+            tseq += wave_sum64(n);
+        }
     }
     const uint64_t T = (uint64_t)tseq * (uint64_t)HG;
     const int bid = blockIdx.x;
@@ -107,13 +126,20 @@ void decode_stream_kernel(const DecodeParams P)
     // locate c_lo: the sequence by a prefix scan over the units' step counts
     // (times HG when the head groups of a sequence are consecutive), then the
     // head group and the step
-    constexpr bool SEQ_MAJOR = PA_STREAM_SEQ_MAJOR != 0;
-    int hg = SEQ_MAJOR ? 0 : (int)(c_lo / (uint64_t)tseq);
+    int hg = SEQ_MAJOR ? 0
+           : c_lo < (1ull << 32) && (uint64_t)tseq < (1ull << 32) ? (int)((uint32_t)c_lo / (uint32_t)tseq)
+                                                                  : (int)(c_lo / (uint64_t)tseq);
     const int64_t r0 = (int64_t)(c_lo - (uint64_t)hg * (uint64_t)tseq);
     const int64_t mult = SEQ_MAJOR ? HG : 1;
     int s = 0;
     int64_t base = 0;
-    for (int b = 0; b < S; b += 64) {
+    if (few) {
+        const uint64_t hit = __ballot(lane < S && incl_lane > r0);
+        const int k = __ffsll((unsigned long long)hit) - 1;
+        s = __builtin_amdgcn_readfirstlane(k);
+        base = uniform64(__shfl(incl_lane - n_lane, k));
+    }
+    for (int b = 0; b < (few ? 0 : S); b += 64) {
         const int i = b + lane;
         const int64_t n = i < S ? mult * max(1, (clamp_ctx(P.ctx[i]) + STEP - 1) / STEP) : 0;
         const int64_t incl = wave_incl_scan64(n, lane);
@@ -147,7 +173,7 @@ void decode_stream_kernel(const DecodeParams P)
         s = __builtin_amdgcn_readfirstlane(s);
         hg = __builtin_amdgcn_readfirstlane(hg);
         j = __builtin_amdgcn_readfirstlane(j);
-        const int ctx = clamp_ctx(P.ctx[s]);
+        const int ctx = few ? __builtin_amdgcn_readlane(ctx_lane, s) : clamp_ctx(P.ctx[s]);
         const int nreal = (ctx + STEP - 1) / STEP;
         const int nsched = max(1, nreal);
         const uint64_t left = c_hi - pos;
