@@ -253,6 +253,13 @@ struct GqaWorker {
     static constexpr int LDS_BYTES = STAGES * TILE_LDS;
     static constexpr int STEP_TOK = GQA_TILE;   // tokens per step of the schedule
     static constexpr int LOADS_PER_TILE = NC + NL;   // vector-memory operations load() issues
+    // In the balanced schedule, one wave per SIMD: the stream kernel's
+    // one-wave workgroups take a quarter of the compute unit's 160 KiB of LDS
+    // each, so four fit.  Two waves on one SIMD do not share it evenly (the
+    // older wave issues first and ends its share far earlier), and the
+    // kernel ended ragged; one wave per SIMD, holding the same tiles in
+    // flight, also halves the waves, the cut units and their pieces.
+    static constexpr int STREAM_LDS_MIN = 160 * 1024 / 4;
     using Ops = GqaOps<T>;
 
     struct Buf {

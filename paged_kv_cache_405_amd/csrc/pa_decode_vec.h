@@ -60,6 +60,7 @@ struct VecWorker {
     static constexpr int SLAB_TOK = NLD * ROWS;      // tokens per step
 
     static constexpr int STEP_TOK = SLAB_TOK;        // tokens per step of the schedule
+    static constexpr int STREAM_LDS_MIN = 0;          // the stream kernel's LDS: its own needs only
     static constexpr int LOADS_PER_TILE = 2 * NLD;   // vector-memory operations load() issues
     static constexpr int LDS_BYTES = 0;              // no LDS staging
     __device__ __forceinline__ void init_lds(unsigned char __attribute__((address_space(3))) *) {}

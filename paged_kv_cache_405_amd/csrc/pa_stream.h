@@ -163,7 +163,10 @@ void decode_stream_kernel(const DecodeParams P)
 
     W wk;
     wk.init_lane(lane);
-    __shared__ __attribute__((aligned(16))) unsigned char lds[W::LDS_BYTES > 0 ? W::LDS_BYTES : 16];
+    // at least W::STREAM_LDS_MIN bytes: a worker may size its workgroups so
+    // that a compute unit holds only a few of them (one wave per SIMD)
+    constexpr int LDS_N = W::LDS_BYTES > W::STREAM_LDS_MIN ? W::LDS_BYTES : W::STREAM_LDS_MIN;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_N > 0 ? LDS_N : 16];
     wk.init_lds((unsigned char __attribute__((address_space(3))) *)lds);
     uint64_t pos = c_lo;
     bool first = true;

@@ -84,12 +84,19 @@ def test_workspace_exact_size():
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(g.q)
     L = B.lib()
-    args = lambda nbytes: (out.data_ptr(), g.q.data_ptr(), g.k_cache.data_ptr(), g.v_cache.data_ptr(),  # noqa: E731
-                           g.tables.data_ptr(), g.ctx.data_ptr(), S, Hq, w.num_kv_heads, D, w.block_size,
-                           w.max_blocks_per_seq, w.num_blocks, ctypes.c_float(w.scale), B.PA_F16, B.PA_LAYOUT_BHTD,
-                           bal, B.PA_KERNEL_AUTO, 0, ws.data_ptr(), nbytes, ctypes.c_void_p(
-                               torch.cuda.current_stream().cuda_stream))
-    assert L.pa_decode_ex(*args(need - 1)) == B.PA_ERR_WORKSPACE
-    assert L.pa_decode_ex(*args(need)) == B.PA_OK
+    args = lambda nbytes, kern: (out.data_ptr(), g.q.data_ptr(), g.k_cache.data_ptr(), g.v_cache.data_ptr(),  # noqa
+                                 g.tables.data_ptr(), g.ctx.data_ptr(), S, Hq, w.num_kv_heads, D, w.block_size,
+                                 w.max_blocks_per_seq, w.num_blocks, ctypes.c_float(w.scale), B.PA_F16,
+                                 B.PA_LAYOUT_BHTD, bal, kern, 0, ws.data_ptr(), nbytes, ctypes.c_void_p(
+                                     torch.cuda.current_stream().cuda_stream))
+    # the query covers whichever kernel the call takes: enough for both, exactly enough for the larger
+    kernels = (B.PA_KERNEL_AUTO, B.PA_KERNEL_VECTOR, B.PA_KERNEL_MFMA)
+    short = [L.pa_decode_ex(*args(need - 1, k)) for k in kernels]
     torch.cuda.synchronize()
-    assert_close(compare(out, oracle_step(w, append=False), "f16"), "f16", "exact workspace")
+    assert B.PA_ERR_WORKSPACE in short and set(short) <= {B.PA_OK, B.PA_ERR_WORKSPACE}
+    ref = oracle_step(w, append=False)
+    for k in kernels:
+        out.fill_(float("nan"))
+        assert L.pa_decode_ex(*args(need, k)) == B.PA_OK
+        torch.cuda.synchronize()
+        assert_close(compare(out, ref, "f16"), "f16", f"exact workspace, kernel {k}")
