@@ -450,7 +450,9 @@ struct GqaWorker {
         vm_wait_tied<NL + LOADS_PER_TILE * BEHIND>(b.k);
     }
 
-    template <int BEHIND>
+    // V_READY: the tile's V is known to be in LDS already (a workgroup that
+    // stages tiles for all its waves has waited and met at a barrier)
+    template <int BEHIND, bool V_READY = false>
     __device__ __forceinline__ void compute(int kt, const Buf &b) {
         gqa_f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -511,7 +513,8 @@ struct GqaWorker {
         // the BEHIND tiles behind) are the only ones left in flight: the
         // compiler cannot see which direct load an LDS read depends on, so
         // the reads are issued by hand after that exact wait.
-        vm_wait<LOADS_PER_TILE * BEHIND>();
+        if constexpr (!V_READY)
+            vm_wait<LOADS_PER_TILE * BEHIND>();
         gqa_u32x2 vb[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -597,6 +600,24 @@ struct GqaWorker {
                 a[16 * t] = acc[t][r];
             if (lr == 0)
                 P.piece_ml[(int64_t)piece * gh + h] = make_float2(mrow[r], lrow[r]);
+        }
+    }
+
+    // bind_rows columns, every key of theirs seen: normalised rows of out
+    // (row q_first + i0 + c / gh, head qh0 + c % gh for column c)
+    __device__ __forceinline__ void finish_rows(const DecodeParams &P, int q_first, int i0, int nq) {
+        finalize();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int c = row_head(r);
+            const int i = i0 + c / gh;
+            if (!owns(r) || i >= nq)
+                continue;
+            const float L = lrow[r];
+            const int64_t base = ((int64_t)(q_first + i) * P.num_q_heads + qh0 + c % gh) * D + lr;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                Store<T>::one(P.out, base + 16 * t, L > 0.f ? acc[t][r] / L : 0.f);
         }
     }
 

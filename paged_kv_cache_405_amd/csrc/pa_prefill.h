@@ -10,12 +10,12 @@
 // tokens in one pass.  Query row i of a chunk of n rows over a context of L
 // tokens sits at position L - n + i and attends tokens 0 .. L - n + i.
 //
-// The per-wave worker is the grouped-query decode worker of pa_decode_gqa.h
+// The per-wave math is the grouped-query decode worker of pa_decode_gqa.h
 // with its 16 score columns taken by (query row, q head) pairs -- 16 / gh rows
 // of the chunk times the gh q heads of one kv head -- each column with its own
-// causal limit.  One workgroup of NW waves per (column tile, head group,
-// sequence) takes the key tiles round robin up to the tile's last position
-// and merges through LDS, as the grid decode kernel does.
+// causal limit.  What differs from decode is where K and V come from: a
+// prefill reads every key tile for many columns, so a workgroup brings each
+// tile into LDS once and all its waves take it from there.
 #pragma once
 
 #include "pa_decode_gqa.h"
@@ -23,17 +23,62 @@
 
 namespace pa {
 
-template <typename T, int D, int BS, int NW, bool STREAM_KV>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(const DecodeParams P)
+// One workgroup of PF_WAVES waves per (group of PF_WAVES column tiles, head
+// group, sequence): wave i owns column tile PF_WAVES * g + i and sees every
+// key tile its columns attend.  A key tile goes from memory into LDS once for
+// the whole workgroup -- its K and V moved by direct-to-LDS loads that the
+// waves share out -- and every wave reads it there:
+//
+//   K  chunk c (32 dims) of the 16 rows is one 1 KiB load: lane i brings row
+//      i / 4, piece p = (i % 4) ^ ((row / 2) % 4) (16 bytes, 8 dims), so that
+//      LDS slot 4 row + (p ^ ((row / 2) % 4)) holds piece p.  The worker's A
+//      operand (lane l: row l % 16, piece l / 16) then reads 16 bytes per lane
+//      with every 8 lanes on 8 different 16-byte bank groups: no conflicts.
+//   V  the worker's own layout (its transposed reads, unchanged).
+//
+// Per tile: each wave waits for its own loads of the tile, the waves meet at a
+// barrier (the tile is complete in LDS, and every wave is done with the tile
+// before, whose slot the next loads then fill), the loads STAGES - 1 tiles
+// ahead go out, and the wave's 16 columns take the tile (worker compute, K
+// fragments from LDS).  Past the last tile the loads repeat the last tile
+// into the free slot, so the wait count is the same on every step.
+//
+// Logical workgroups are XCD-major (dispatch puts workgroup b on XCD b % 8):
+// the column groups of one (head group, sequence) are consecutive and run
+// together on one XCD, whose L2 then serves their re-reads of the same K/V.
+constexpr int PF_WAVES = 4;
+
+template <typename T, int D, int BS, bool STREAM_KV>
+struct PrefillTiles {
+    using W = GqaWorker<T, D, BS, STREAM_KV>;
+    static constexpr int NC = W::NC;                    // K chunks (and loads) per tile
+    static constexpr int NL = W::NL;                    // V loads per tile
+    static constexpr int K_BYTES = NC * 1024;
+    static constexpr int BYTES = K_BYTES + W::TILE_LDS; // one slot: K, then V
+    static constexpr int LOADS = NC + NL;
+    static constexpr int PER_WAVE = LOADS / PF_WAVES;
+    static constexpr int STAGES = D <= 128 ? 3 : 2;
+    static_assert(LOADS % PF_WAVES == 0, "the loads of a tile share out evenly");
+};
+
+template <typename T, int D, int BS, bool STREAM_KV>
+__global__ __launch_bounds__(PF_WAVES * 64) void prefill_kernel(const DecodeParams P, int col_groups, int total_wg)
 {
     static_assert(D % 128 == 0, "the matrix-core worker needs head_dim 128 or 256");
-    using W = GqaWorker<T, D, BS, STREAM_KV>;
-    constexpr int MERGE_BYTES = NW * 16 * (D + 2) * 4;
-    constexpr int LDS_TOTAL = NW * W::LDS_BYTES > MERGE_BYTES ? NW * W::LDS_BYTES : MERGE_BYTES;
+    using PT = PrefillTiles<T, D, BS, STREAM_KV>;
+    using W = typename PT::W;
+    constexpr int STAGES = PT::STAGES;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[STAGES * PT::BYTES];
 
-    const int ct = blockIdx.x;
-    const int hg = blockIdx.y;
-    const int s = blockIdx.z;
+    const int per_xcd = (total_wg + 7) / 8;
+    const int lg_id = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (lg_id >= total_wg)
+        return;
+    const int HG = P.num_kv_heads * P.group_split;
+    const int cg = lg_id % col_groups;
+    const int hg = (lg_id / col_groups) % HG;
+    const int s = lg_id / col_groups / HG;
+
     int ctx = P.ctx[s];
     const int cap = P.max_blocks * BS;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
@@ -44,64 +89,106 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const DecodeParams P)
         return;
     nq = nq > P.total_q - q_first ? P.total_q - q_first : nq;
     const int gh = P.group / P.group_split;
-    const int i0 = ct * (GQA_TILE / gh);
-    if (i0 >= nq)
+    const int rows = GQA_TILE / gh;                       // query rows per column tile
+    const int i0g = cg * PF_WAVES * rows;
+    if (i0g >= nq)
         return;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_TOTAL];
-
+    const int i0 = i0g + wave * rows;
+    const bool active = i0 < nq;
     W w;
     w.init_lane(lane);
-    w.init_lds((unsigned char PA_LDS *)lds + wave * W::LDS_BYTES);
-    w.bind_rows(P, s, hg, ctx, q_first, nq, i0);
-    const int k1 = (w.t_last + GQA_TILE - 1) / GQA_TILE;
-    w.reset();
-    w.run(wave, k1, NW);
+    w.bind_rows(P, s, hg, ctx, q_first, nq, active ? i0 : i0g);
+    // key tiles of the group: up to the last position any of its rows attends
+    const int last_row = min(i0g + PF_WAVES * rows, nq) - 1;
+    const int t_end = min(ctx, max(0, ctx - nq + last_row + 1));
+    const int n_tiles = (t_end + GQA_TILE - 1) / GQA_TILE;
+    const int my_tiles = active ? (w.t_last + GQA_TILE - 1) / GQA_TILE : 0;
 
-    // every load of every wave has landed before the tile slots become the merge area
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    float *sm_m = reinterpret_cast<float *>(lds);
-    float *sm_l = sm_m + NW * 16;
-    float *sm_acc = sm_l + NW * 16;
-    w.export_lds(sm_m + wave * 16, sm_l + wave * 16, sm_acc + wave * 16 * D);
-    __syncthreads();
+    unsigned char PA_LDS *base = (unsigned char PA_LDS *)lds;
+    // K source rows of this lane (K loads: row i / 4, swizzled piece)
+    const int k_row = lane >> 2;
+    const int k_piece = (lane & 3) ^ ((k_row >> 1) & 3);
+    // K slot of this lane's A operand (row lane % 16, piece lane / 16)
+    const int a_row = lane & 15, a_piece = lane >> 4;
+    const int a_off = 16 * (4 * a_row + (a_piece ^ ((a_row >> 1) & 3)));
 
-    for (int idx = threadIdx.x; idx < w.ncols * D; idx += NW * 64) {
-        const int g = idx / D;
-        const int d = idx - g * D;
-        const int i = i0 + g / gh;
-        if (i >= nq)
-            continue;
-        float M = sm_m[g];
+    auto issue = [&](int kt, int st) {
+        const int2 pp = w.tile_phys(kt);
+        const bool oka = (unsigned)pp.x < (unsigned)w.num_blocks;
+        const bool okb = (unsigned)pp.y < (unsigned)w.num_blocks;
+        const int t0 = kt * GQA_TILE;
+        const uint32_t slot = (uint32_t)(uintptr_t)(base + st * PT::BYTES);
 #pragma unroll
-        for (int v = 1; v < NW; ++v)
-            M = fmaxf(M, sm_m[v * 16 + g]);
-        float L = 0.f, A = 0.f;
-#pragma unroll
-        for (int v = 0; v < NW; ++v) {
-            const float c = fast_exp2(sm_m[v * 16 + g] - M);
-            L = fmaf(sm_l[v * 16 + g], c, L);
-            A = fmaf(sm_acc[(v * 16 + g) * D + d], c, A);
+        for (int p = 0; p < PT::PER_WAVE; ++p) {
+            const int j = wave * PT::PER_WAVE + p;          // wave-uniform
+            if (j < PT::NC) {
+                // K chunk j: this lane's row and piece
+                const bool second = BS < GQA_TILE && k_row >= BS;
+                const int64_t blk = second ? (okb ? pp.y : 0) : (oka ? pp.x : 0);
+                const int in_row = BS < GQA_TILE ? (k_row & (BS - 1)) : (t0 % BS) + k_row;
+                const char *src = w.kpool + blk * w.blk_bytes + (int64_t)in_row * w.tok_bytes + 64 * j + 16 * k_piece;
+                load_lds_asm<STREAM_KV>(src, slot + j * 1024);
+            } else {
+                // V load i, as the worker lays V out: token 4 grp + lane % 4, chunk lane / 4
+                const int i = j - PT::NC;
+                const int grp = i / (D / 128), half = i % (D / 128);
+                const bool second = BS < GQA_TILE && 4 * grp >= BS;
+                const int64_t blk = second ? (okb ? pp.y : 0) : (oka ? pp.x : 0);
+                const int in_row = BS < GQA_TILE ? (4 * grp) & (BS - 1) : (t0 % BS) + 4 * grp;
+                const char *src = w.vpool + blk * w.blk_bytes + (int64_t)in_row * w.tok_bytes + 256 * half + w.v_src;
+                load_lds_asm<STREAM_KV>(src, slot + PT::K_BYTES + i * W::LOAD_LDS);
+            }
         }
-        const int64_t row = (int64_t)(q_first + i) * P.num_q_heads + w.qh0 + g % gh;
-        Store<T>::one(P.out, row * D + d, L > 0.f ? A / L : 0.f);
-    }
-}
+    };
 
-constexpr int PREFILL_WAVES = 4;
+    w.reset();
+    if (n_tiles > 0) {
+#pragma unroll
+        for (int i = 0; i < STAGES - 1; ++i)
+            issue(min(i, n_tiles - 1), i);
+        for (int t = 0; t < n_tiles; ++t) {
+            vm_wait<PT::PER_WAVE * (STAGES - 2)>();        // this wave's loads of tile t
+            asm volatile("s_barrier" ::: "memory");       // tile t complete; tile t - 1 done by all
+            issue(min(t + STAGES - 1, n_tiles - 1), (t + STAGES - 1) % STAGES);
+            if (t < my_tiles) {
+                const unsigned char PA_LDS *st = base + (t % STAGES) * PT::BYTES;
+                typename W::Buf b;
+#pragma unroll
+                for (int c = 0; c < PT::NC; ++c)
+                    b.k[c] = *reinterpret_cast<const gqa_u32x4 PA_LDS *>(st + c * 1024 + a_off);
+                b.v = const_cast<unsigned char PA_LDS *>(st + PT::K_BYTES);
+                const int2 pp = w.tile_phys(t);
+                b.oka = (unsigned)pp.x < (unsigned)w.num_blocks;
+                b.okb = (unsigned)pp.y < (unsigned)w.num_blocks;
+                w.template compute<0, true>(t, b);
+            }
+        }
+        // every load into LDS has landed before the workgroup ends
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    if (active)
+        w.finish_rows(P, q_first, i0, nq);
+}
 
 template <typename T, int D, int BS>
 hipError_t launch_prefill_shape(const DecodeParams &p, int max_query_len, hipStream_t st)
 {
     const int rows = GQA_TILE / (p.group / p.group_split);
-    dim3 grid((max_query_len + rows - 1) / rows, p.num_kv_heads * p.group_split, p.num_seqs);
+    const int col_tiles = (max_query_len + rows - 1) / rows;
+    const int col_groups = (col_tiles + PF_WAVES - 1) / PF_WAVES;
+    const long long total = (long long)col_groups * p.num_kv_heads * p.group_split * p.num_seqs;
+    if (total > (1LL << 30))
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((total + 7) / 8 * 8));
     if (p.kv_cached)
-        hipLaunchKernelGGL((prefill_kernel<T, D, BS, PREFILL_WAVES, false>), grid, dim3(PREFILL_WAVES * 64), 0, st, p);
+        hipLaunchKernelGGL((prefill_kernel<T, D, BS, false>), grid, dim3(PF_WAVES * 64), 0, st, p, col_groups,
+                           (int)total);
     else
-        hipLaunchKernelGGL((prefill_kernel<T, D, BS, PREFILL_WAVES, true>), grid, dim3(PREFILL_WAVES * 64), 0, st, p);
+        hipLaunchKernelGGL((prefill_kernel<T, D, BS, true>), grid, dim3(PF_WAVES * 64), 0, st, p, col_groups,
+                           (int)total);
     return hipGetLastError();
 }
 
