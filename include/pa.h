@@ -223,6 +223,8 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
  *   max_query_len   the most rows of any sequence (sizes the grid; rows past
  *                   it are not computed)
  *   other arguments as for pa_decode_ex; flags: 0 or PA_DECODE_SHARED_BLOCKS
+ *                   (accepted; prefill always loads K/V with the caches'
+ *                   normal policy, since every tile is read for many rows)
  *
  * Runs on the matrix cores: f16 or bf16, head_dim 128 or 256, at most 16 q
  * heads per kv head or a multiple of 16; otherwise PA_ERR_UNSUPPORTED.  No

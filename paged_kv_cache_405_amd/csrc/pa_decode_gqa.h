@@ -239,6 +239,12 @@ __device__ __forceinline__ void lgkm_wait_tied(gqa_u32x2 (&v)[16]) {
                    "+v"(v[15])
                  :: "memory");
 }
+// two sets of reads, each held by a wait of its own (the first retires all)
+template <int N>
+__device__ __forceinline__ void lgkm_wait_tied(gqa_u32x2 (&a)[N], gqa_u32x2 (&b)[N]) {
+    lgkm_wait_tied(a);
+    lgkm_wait_tied(b);
+}
 
 template <typename T, int D, int BS, bool STREAM_KV>
 struct GqaWorker {
@@ -537,6 +543,113 @@ struct GqaWorker {
                 acc[t] = Ops::pv(phi, vb[t], acc[t]);
                 acc[t] = Ops::pv(plo, vb[t], acc[t]);
             }
+        }
+    }
+
+    // Two consecutive key tiles (kt, kt + 1) whose K fragments and V are in
+    // LDS (a workgroup that stages tiles for its waves), with the weighted
+    // sums done by 16x16x32 products: the A operand of one product takes the
+    // lane's four probabilities of each tile (k slots 8g + r and 8g + 4 + r
+    // for tokens 4g + r of the first and of the second tile, g = lane / 16),
+    // and the B operand the two transposed reads of those tokens' V rows, in
+    // the same order -- one product where the single-tile path makes two.
+    // HILO: P as hi + lo (two products); otherwise P is rounded once to the
+    // storage type and the running sum adds the rounded values, so that the
+    // weights the products use are exactly the ones normalised by.
+    template <bool HILO>
+    __device__ __forceinline__ void compute_pair(int kt, const Buf &b0, const Buf &b1) {
+        gqa_f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            sc0 = Ops::score(make_uint4(b0.k[c].x, b0.k[c].y, b0.k[c].z, b0.k[c].w), qb[c], sc0);
+            sc1 = Ops::score(make_uint4(b1.k[c].x, b1.k[c].y, b1.k[c].z, b1.k[c].w), qb[c], sc1);
+        }
+        float sv[8];
+        uint32_t keep[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+        bool any_masked = false;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const Buf &b = h ? b1 : b0;
+            const gqa_f32x4 &sc = h ? sc1 : sc0;
+            const int t0 = (kt + h) * GQA_TILE;
+            const int tv = t0 + 4 * lg;
+            const bool full = b.oka && b.okb && t0 >= t_lo && t0 + GQA_TILE <= t_full;
+            const bool okv = (BS < GQA_TILE && 4 * lg >= BS) ? b.okb : b.oka;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sv[4 * h + r] = sc[r] * scale_log2;
+            if (!full) {
+                any_masked = true;
+                bool readable[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    readable[r] = okv && tv + r >= t_lo && tv + r < t_vlim;
+                    sv[4 * h + r] = readable[r] && tv + r < t_hi ? sv[4 * h + r] : -INFINITY;
+                }
+                keep[2 * h] = (readable[0] ? 0x0000ffffu : 0u) | (readable[1] ? 0xffff0000u : 0u);
+                keep[2 * h + 1] = (readable[2] ? 0x0000ffffu : 0u) | (readable[3] ? 0xffff0000u : 0u);
+            }
+        }
+        float mx = sv[0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r)
+            mx = fmaxf(mx, sv[r]);
+        mx = max_token_groups(mx);
+        const bool grow = mx > m + GQA_RESCALE_LOG2;
+        if (__any(grow)) {
+            const float mn = grow ? mx : m;
+            const float alpha = fast_exp2(m - mn);
+            lp *= alpha;
+            m = mn;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * lg + r);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    acc[t][r] *= ar;
+            }
+        }
+        float pr[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            pr[r] = fast_exp2(sv[r] - m);
+        const uint4 phi = make_uint4(Ops::pack(pr[0], pr[1]), Ops::pack(pr[2], pr[3]), Ops::pack(pr[4], pr[5]),
+                                     Ops::pack(pr[6], pr[7]));
+        float w[8];
+        Ops::unpack(phi.x, w[0], w[1]);
+        Ops::unpack(phi.y, w[2], w[3]);
+        Ops::unpack(phi.z, w[4], w[5]);
+        Ops::unpack(phi.w, w[6], w[7]);
+        uint4 plo = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (HILO) {
+            lp += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+            plo = make_uint4(Ops::pack(pr[0] - w[0], pr[1] - w[1]), Ops::pack(pr[2] - w[2], pr[3] - w[3]),
+                             Ops::pack(pr[4] - w[4], pr[5] - w[5]), Ops::pack(pr[6] - w[6], pr[7] - w[7]));
+        } else {
+            lp += ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+        }
+        gqa_u32x2 va[NT], vb[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            va[t] = read_tr_asm(b0.v + tr_off + ((16 * t) / 128) * LOAD_LDS, (t % 8) * 128);
+            vb[t] = read_tr_asm(b1.v + tr_off + ((16 * t) / 128) * LOAD_LDS, (t % 8) * 128);
+        }
+        lgkm_wait_tied(va, vb);
+        if (any_masked) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                va[t].x &= keep[0];
+                va[t].y &= keep[1];
+                vb[t].x &= keep[2];
+                vb[t].y &= keep[3];
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint4 vop = make_uint4(va[t].x, va[t].y, vb[t].x, vb[t].y);
+            acc[t] = Ops::score(phi, vop, acc[t]);
+            if constexpr (HILO)
+                acc[t] = Ops::score(plo, vop, acc[t]);
         }
     }
 

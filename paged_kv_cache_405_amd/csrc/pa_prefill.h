@@ -18,6 +18,8 @@
 // tile into LDS once and all its waves take it from there.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_decode_gqa.h"
 #include "pa_device.h"
 
@@ -36,17 +38,26 @@ namespace pa {
 //      with every 8 lanes on 8 different 16-byte bank groups: no conflicts.
 //   V  the worker's own layout (its transposed reads, unchanged).
 //
-// Per tile: each wave waits for its own loads of the tile, the waves meet at a
-// barrier (the tile is complete in LDS, and every wave is done with the tile
-// before, whose slot the next loads then fill), the loads STAGES - 1 tiles
-// ahead go out, and the wave's 16 columns take the tile (worker compute, K
-// fragments from LDS).  Past the last tile the loads repeat the last tile
-// into the free slot, so the wait count is the same on every step.
+// A slot holds a pair of tiles, which the worker takes in one step
+// (compute_pair: 16x16x32 products for the weighted sums as well as for the
+// scores).  Per step: each wave waits for its own loads of the slot, the
+// waves meet at a barrier (the slot is complete in LDS, and every wave is done
+// with the slot before, which the next loads then fill), the loads STAGES - 1
+// slots ahead go out, and the wave's 16 columns take the pair (K fragments
+// from LDS).  Past the last pair the loads repeat the last one into the free
+// slot, so the wait count is the same on every step; a tile past the last is
+// read as unmapped, so it contributes nothing.
 //
 // Logical workgroups are XCD-major (dispatch puts workgroup b on XCD b % 8):
 // the column groups of one (head group, sequence) are consecutive and run
 // together on one XCD, whose L2 then serves their re-reads of the same K/V.
-constexpr int PF_WAVES = 4;
+#ifndef PA_PF_WAVES
+#define PA_PF_WAVES 8           // waves (16-column tiles) per workgroup
+#endif
+#ifndef PA_PF_STAGES
+#define PA_PF_STAGES 2          // slots (tile pairs) in rotation, head_dim 128
+#endif
+constexpr int PF_WAVES = PA_PF_WAVES;
 
 template <typename T, int D, int BS, bool STREAM_KV>
 struct PrefillTiles {
@@ -54,11 +65,15 @@ struct PrefillTiles {
     static constexpr int NC = W::NC;                    // K chunks (and loads) per tile
     static constexpr int NL = W::NL;                    // V loads per tile
     static constexpr int K_BYTES = NC * 1024;
-    static constexpr int BYTES = K_BYTES + W::TILE_LDS; // one slot: K, then V
-    static constexpr int LOADS = NC + NL;
+    static constexpr int TILE_BYTES = K_BYTES + W::TILE_LDS;   // one tile: K, then V
+    static constexpr int BYTES = 2 * TILE_BYTES;        // one slot: a pair of tiles
+    static constexpr int TILE_LOADS = NC + NL;
+    static constexpr int LOADS = 2 * TILE_LOADS;
     static constexpr int PER_WAVE = LOADS / PF_WAVES;
-    static constexpr int STAGES = D <= 128 ? 3 : 2;
-    static_assert(LOADS % PF_WAVES == 0, "the loads of a tile share out evenly");
+    static constexpr int STAGES = D <= 128 ? PA_PF_STAGES : 2;
+    static_assert(LOADS % PF_WAVES == 0, "the loads of a slot share out evenly");
+    // bf16 keeps P as hi + lo (8 significant bits would not meet the accuracy bound); f16 rounds it once
+    static constexpr bool HILO = std::is_same<T, bf16_t>::value;
 };
 
 template <typename T, int D, int BS, bool STREAM_KV>
@@ -115,55 +130,66 @@ __global__ __launch_bounds__(PF_WAVES * 64) void prefill_kernel(const DecodePara
     const int a_row = lane & 15, a_piece = lane >> 4;
     const int a_off = 16 * (4 * a_row + (a_piece ^ ((a_row >> 1) & 3)));
 
-    auto issue = [&](int kt, int st) {
-        const int2 pp = w.tile_phys(kt);
-        const bool oka = (unsigned)pp.x < (unsigned)w.num_blocks;
-        const bool okb = (unsigned)pp.y < (unsigned)w.num_blocks;
-        const int t0 = kt * GQA_TILE;
+    // slot st <- tiles 2 step and 2 step + 1 (a tile past the last repeats the last: same bytes, never used)
+    auto issue = [&](int step, int st) {
         const uint32_t slot = (uint32_t)(uintptr_t)(base + st * PT::BYTES);
 #pragma unroll
         for (int p = 0; p < PT::PER_WAVE; ++p) {
             const int j = wave * PT::PER_WAVE + p;          // wave-uniform
-            if (j < PT::NC) {
-                // K chunk j: this lane's row and piece
+            const int h = j / PT::TILE_LOADS, jj = j % PT::TILE_LOADS;
+            const int kt = min(2 * step + h, n_tiles - 1);
+            const int2 pp = w.tile_phys(kt);
+            const bool oka = (unsigned)pp.x < (unsigned)w.num_blocks;
+            const bool okb = (unsigned)pp.y < (unsigned)w.num_blocks;
+            const int t0 = kt * GQA_TILE;
+            const uint32_t tslot = slot + h * PT::TILE_BYTES;
+            if (jj < PT::NC) {
+                // K chunk jj: this lane's row and piece
                 const bool second = BS < GQA_TILE && k_row >= BS;
                 const int64_t blk = second ? (okb ? pp.y : 0) : (oka ? pp.x : 0);
                 const int in_row = BS < GQA_TILE ? (k_row & (BS - 1)) : (t0 % BS) + k_row;
-                const char *src = w.kpool + blk * w.blk_bytes + (int64_t)in_row * w.tok_bytes + 64 * j + 16 * k_piece;
-                load_lds_asm<STREAM_KV>(src, slot + j * 1024);
+                const char *src = w.kpool + blk * w.blk_bytes + (int64_t)in_row * w.tok_bytes + 64 * jj + 16 * k_piece;
+                load_lds_asm<STREAM_KV>(src, tslot + jj * 1024);
             } else {
                 // V load i, as the worker lays V out: token 4 grp + lane % 4, chunk lane / 4
-                const int i = j - PT::NC;
+                const int i = jj - PT::NC;
                 const int grp = i / (D / 128), half = i % (D / 128);
                 const bool second = BS < GQA_TILE && 4 * grp >= BS;
                 const int64_t blk = second ? (okb ? pp.y : 0) : (oka ? pp.x : 0);
                 const int in_row = BS < GQA_TILE ? (4 * grp) & (BS - 1) : (t0 % BS) + 4 * grp;
                 const char *src = w.vpool + blk * w.blk_bytes + (int64_t)in_row * w.tok_bytes + 256 * half + w.v_src;
-                load_lds_asm<STREAM_KV>(src, slot + PT::K_BYTES + i * W::LOAD_LDS);
+                load_lds_asm<STREAM_KV>(src, tslot + PT::K_BYTES + i * W::LOAD_LDS);
             }
         }
     };
+    // the wave's view of tile kt in slot st: K fragments from LDS, V in place; a
+    // tile past the last is unmapped (masked out)
+    auto view = [&](int kt, const unsigned char PA_LDS *ts, typename W::Buf &b) {
+#pragma unroll
+        for (int c = 0; c < PT::NC; ++c)
+            b.k[c] = *reinterpret_cast<const gqa_u32x4 PA_LDS *>(ts + c * 1024 + a_off);
+        b.v = const_cast<unsigned char PA_LDS *>(ts + PT::K_BYTES);
+        const int2 pp = kt < n_tiles ? w.tile_phys(kt) : make_int2(-1, -1);
+        b.oka = (unsigned)pp.x < (unsigned)w.num_blocks;
+        b.okb = (unsigned)pp.y < (unsigned)w.num_blocks;
+    };
 
     w.reset();
-    if (n_tiles > 0) {
+    const int n_steps = (n_tiles + 1) / 2;
+    if (n_steps > 0) {
 #pragma unroll
         for (int i = 0; i < STAGES - 1; ++i)
-            issue(min(i, n_tiles - 1), i);
-        for (int t = 0; t < n_tiles; ++t) {
-            vm_wait<PT::PER_WAVE * (STAGES - 2)>();        // this wave's loads of tile t
-            asm volatile("s_barrier" ::: "memory");       // tile t complete; tile t - 1 done by all
-            issue(min(t + STAGES - 1, n_tiles - 1), (t + STAGES - 1) % STAGES);
-            if (t < my_tiles) {
-                const unsigned char PA_LDS *st = base + (t % STAGES) * PT::BYTES;
-                typename W::Buf b;
-#pragma unroll
-                for (int c = 0; c < PT::NC; ++c)
-                    b.k[c] = *reinterpret_cast<const gqa_u32x4 PA_LDS *>(st + c * 1024 + a_off);
-                b.v = const_cast<unsigned char PA_LDS *>(st + PT::K_BYTES);
-                const int2 pp = w.tile_phys(t);
-                b.oka = (unsigned)pp.x < (unsigned)w.num_blocks;
-                b.okb = (unsigned)pp.y < (unsigned)w.num_blocks;
-                w.template compute<0, true>(t, b);
+            issue(min(i, n_steps - 1), i);
+        for (int step = 0; step < n_steps; ++step) {
+            vm_wait<PT::PER_WAVE * (STAGES - 2)>();        // this wave's loads of this step's slot
+            asm volatile("s_barrier" ::: "memory");       // the slot complete; the one before done by all
+            issue(min(step + STAGES - 1, n_steps - 1), (step + STAGES - 1) % STAGES);
+            if (2 * step < my_tiles) {
+                const unsigned char PA_LDS *ss = base + (step % STAGES) * PT::BYTES;
+                typename W::Buf b0, b1;
+                view(2 * step, ss, b0);
+                view(2 * step + 1, ss + PT::TILE_BYTES, b1);
+                w.template compute_pair<PT::HILO>(2 * step, b0, b1);
             }
         }
         // every load into LDS has landed before the workgroup ends
@@ -183,12 +209,10 @@ hipError_t launch_prefill_shape(const DecodeParams &p, int max_query_len, hipStr
     if (total > (1LL << 30))
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)((total + 7) / 8 * 8));
-    if (p.kv_cached)
-        hipLaunchKernelGGL((prefill_kernel<T, D, BS, false>), grid, dim3(PF_WAVES * 64), 0, st, p, col_groups,
-                           (int)total);
-    else
-        hipLaunchKernelGGL((prefill_kernel<T, D, BS, true>), grid, dim3(PF_WAVES * 64), 0, st, p, col_groups,
-                           (int)total);
+    // every column group of a (head group, sequence) reads the same key tiles:
+    // K and V are loaded with the caches' normal policy, whatever the flags say
+    hipLaunchKernelGGL((prefill_kernel<T, D, BS, false>), grid, dim3(PF_WAVES * 64), 0, st, p, col_groups,
+                       (int)total);
     return hipGetLastError();
 }
 
