@@ -91,7 +91,8 @@ pa_status pa_swap_blocks(void *dst_k, void *dst_v, const void *src_k, const void
  *   - a forked request shares all its parent's blocks; a request that
  *     appends into a shared, partly filled last block first gets a private
  *     copy of it (one (source, destination) pair to copy);
- *   - * a block returns to its pool when no request holds it;
+ *   - * a block returns to its pool when no request holds it (a block in
+ *     the prefix cache stays cached until it is taken, see below);
  *   - * swapping out gives a request CPU copies of all its blocks (a GPU
  *     block that other requests hold stays on the GPU for them); swapping in
  *     gives it fresh GPU blocks;
@@ -139,7 +140,42 @@ pa_status pa_bm_swap_in(pa_block_manager *bm, int64_t seq, int32_t *pairs, int m
  */
 pa_status pa_bm_block_tables(pa_block_manager *bm, const int64_t *seqs, int n, int max_blocks, int32_t *tables,
                              int32_t *context_lens);
-/* free blocks of a pool (0 = GPU, 1 = CPU) */
+/*
+ * Automatic prefix caching ("vLLM 与 PagedAttention" section 四, "Prefix
+ * Caching：复用 system prompt 的 KV"): the KV of a prompt's prefix stays
+ * cached, and a later request whose prompt starts the same way reuses it and
+ * computes only the rest.  Readings where the pages are silent:
+ *   - the unit is a full block, known by its whole token prefix (a block's
+ *     chain hash covers every token before it; a hit also checks the
+ *     block's own tokens and its parent's hash); partly filled blocks are
+ *     never cached;
+ *   - a full block joins the cache as soon as its request has all its tokens
+ *     (pa_bm_append_tokens; the caller writes their KV with
+ *     pa_reshape_and_cache before another request looks the prompt up); if
+ *     that prefix is cached already, the block stays private;
+ *   - a cached block that no request holds stays cached and counts as free:
+ *     an allocation takes a free block if there is one, else the cached
+ *     block released longest ago (ties: lowest index), which leaves the
+ *     cache; a request's blocks are released last block first;
+ *   - a request whose tokens were not all given (pa_bm_append) adds nothing
+ *     to the cache from then on.
+ */
+/*
+ * A new request (a new id) for prompt[n]: its table starts with the cached
+ * blocks the prompt begins with -- at most (n - 1) / block_size of them, so at
+ * least one prompt token is left to compute -- and *cached_tokens receives
+ * how many tokens that covers (a multiple of block_size).  The caller then
+ * appends the rest of the prompt with pa_bm_append_tokens and computes it.
+ */
+pa_status pa_bm_add_cached(pa_block_manager *bm, int64_t seq, const int32_t *prompt, int n, int *cached_tokens);
+/* pa_bm_append, with the tokens given (int32 [n], host), so that the blocks they fill can be cached */
+pa_status pa_bm_append_tokens(pa_block_manager *bm, int64_t seq, const int32_t *tokens, int n, int64_t *slots,
+                              int32_t *copies, int max_copies, int *num_copies);
+/* GPU blocks in the prefix cache, and how many of them no request holds */
+pa_status pa_bm_cache_stats(pa_block_manager *bm, int *cached_blocks, int *evictable_blocks);
+
+/* blocks an allocation from a pool (0 = GPU, 1 = CPU) can take: free ones and,
+ * on the GPU, cached ones no request holds */
 pa_status pa_bm_num_free(pa_block_manager *bm, int pool, int *out);
 /* requests holding a block of a pool (0 = GPU, 1 = CPU) */
 pa_status pa_bm_ref_count(pa_block_manager *bm, int pool, int block, int *out);

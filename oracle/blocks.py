@@ -78,6 +78,10 @@ class BlockManagerModel:
         self.ref[pool][b] -= 1
         assert self.ref[pool][b] >= 0
 
+    def _available(self, pool: str) -> int:
+        """Blocks an allocation can take."""
+        return len(self.free_blocks(pool))
+
     # -- requests -----------------------------------------------------------
     def add(self, sid: int) -> None:
         assert sid not in self.tables
@@ -102,7 +106,7 @@ class BlockManagerModel:
     def append(self, sid: int, n: int):
         """Grow a request by n tokens: (slot of each new token, copies (src, dst))."""
         assert self.where[sid] == "gpu"
-        if self.blocks_needed(sid, n) > len(self.free_blocks("gpu")):
+        if self.blocks_needed(sid, n) > self._available("gpu"):
             raise NoBlocks("gpu")
         table, bs = self.tables[sid], self.bs
         slots, copies = [], []
@@ -120,8 +124,9 @@ class BlockManagerModel:
         return slots, copies
 
     def free(self, sid: int) -> None:
+        """Drop a request; its blocks are released last block first."""
         pool = self.where.pop(sid)
-        for b in self.tables.pop(sid):
+        for b in reversed(self.tables.pop(sid)):
             self._drop(pool, b)
         del self.lens[sid]
 
@@ -129,14 +134,12 @@ class BlockManagerModel:
         """Move a request to CPU blocks: (gpu block, cpu block) pairs to copy."""
         assert self.where[sid] == "gpu"
         table = self.tables[sid]
-        if len(table) > len(self.free_blocks("cpu")):
+        if len(table) > self._available("cpu"):
             raise NoBlocks("cpu")
-        pairs = []
-        for j, b in enumerate(table):
-            c = self._take("cpu")
-            pairs.append((b, c))
+        pairs = [(b, self._take("cpu")) for b in table]
+        for b in reversed(table):                   # GPU blocks released last block first
             self._drop("gpu", b)
-            table[j] = c
+        table[:] = [c for _, c in pairs]
         self.where[sid] = "cpu"
         return pairs
 
@@ -144,7 +147,7 @@ class BlockManagerModel:
         """Move a request back to fresh GPU blocks: (cpu block, gpu block) pairs."""
         assert self.where[sid] == "cpu"
         table = self.tables[sid]
-        if len(table) > len(self.free_blocks("gpu")):
+        if len(table) > self._available("gpu"):
             raise NoBlocks("gpu")
         pairs = []
         for j, c in enumerate(table):

@@ -91,6 +91,12 @@ def lib():
             L.pa_bm_append.argtypes = [vp, i64, i32, pi64, pi32, i32, pi32]
             L.pa_bm_free.restype = i32
             L.pa_bm_free.argtypes = [vp, i64]
+            L.pa_bm_add_cached.restype = i32
+            L.pa_bm_add_cached.argtypes = [vp, i64, pi32, i32, pi32]
+            L.pa_bm_append_tokens.restype = i32
+            L.pa_bm_append_tokens.argtypes = [vp, i64, pi32, i32, pi64, pi32, i32, pi32]
+            L.pa_bm_cache_stats.restype = i32
+            L.pa_bm_cache_stats.argtypes = [vp, pi32, pi32]
             for f in (L.pa_bm_swap_out, L.pa_bm_swap_in):
                 f.restype = i32
                 f.argtypes = [vp, i64, pi32, i32, pi32]
@@ -387,6 +393,33 @@ class BlockManager:
         nc = ctypes.c_int32(0)
         self._call("pa_bm_append", seq, n, slots, copies, 1, ctypes.byref(nc))
         return list(slots[:n]), [(copies[2 * i], copies[2 * i + 1]) for i in range(nc.value)]
+
+    def append_tokens(self, seq: int, tokens):
+        """append() with the token ids given, so that the blocks they fill can be cached."""
+        tokens = [int(t) for t in tokens]
+        n = len(tokens)
+        toks = (ctypes.c_int32 * max(n, 1))(*tokens)
+        slots = (ctypes.c_int64 * max(n, 1))()
+        copies = (ctypes.c_int32 * 2)()
+        nc = ctypes.c_int32(0)
+        self._call("pa_bm_append_tokens", seq, toks, n, slots, copies, 1, ctypes.byref(nc))
+        return list(slots[:n]), [(copies[2 * i], copies[2 * i + 1]) for i in range(nc.value)]
+
+    def add_cached(self, seq: int, prompt) -> int:
+        """A new request whose table starts with the cached blocks `prompt` begins
+        with; returns the prompt tokens already cached."""
+        prompt = [int(t) for t in prompt]
+        n = len(prompt)
+        toks = (ctypes.c_int32 * max(n, 1))(*prompt)
+        hit = ctypes.c_int32(0)
+        self._call("pa_bm_add_cached", seq, toks, n, ctypes.byref(hit))
+        return hit.value
+
+    def cache_stats(self):
+        """(cached GPU blocks, cached blocks no request holds)."""
+        c, e = ctypes.c_int32(0), ctypes.c_int32(0)
+        self._call("pa_bm_cache_stats", ctypes.byref(c), ctypes.byref(e))
+        return c.value, e.value
 
     def free(self, seq: int):
         self._call("pa_bm_free", seq)
