@@ -50,7 +50,8 @@ def parse(argv=None):
                     help="decode kernel family (pa_kernel): auto picks matrix cores for grouped-query heads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["decode", "prefill", "copy_blocks", "swap_out", "swap_in"], default="decode",
+    ap.add_argument("--op", choices=["decode", "prefill", "prefix_cache", "copy_blocks", "swap_out", "swap_in"],
+                    default="decode",
                     help="decode (the default step); prefill (a 512-token chunk per sequence over a 1536-token "
                          "cached history); or one of the block moves of the paging system: copy_blocks (copy on "
                          "write inside the GPU pools), swap_out / swap_in (GPU pools <-> pinned host pools)")
@@ -62,6 +63,123 @@ def parse(argv=None):
 
 HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 MFMA_F16_PEAK_TFLOPS = 2500.0   # dense f16 / bf16 matrix-core peak of the MI355X
+
+
+def prefix_cache_step(args):
+    """Automatic prefix caching on the pages' customer-service case, at the shared-prefix workload's scale:
+    128 requests whose prompts are one 1504-token system prompt plus 8-200 tokens of their own (32 x 128 MHA
+    heads, fp16, block size 16).  The first request computes its whole prompt; then the other 127 are
+    admitted and prefilled, with the cache (the library's block manager: they reuse the 94 system-prompt
+    blocks and compute only their own tokens) and without it (every prompt computed in full).  Host: the
+    library's manager admitting a request (pa_bm_add_cached + pa_bm_append_tokens), the oracle's model
+    beside it."""
+    import torch
+    from paged_kv_cache_405_amd import binding as B
+    from oracle.prefix_cache import PrefixCacheModel
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+    S, sys_len, H, D, bs = 128, 1504, 32, 128, 16
+    rng = np.random.default_rng(31)
+    system = rng.integers(0, 32000, sys_len).astype(np.int32)
+    own = rng.integers(8, 201, S)
+    prompts = [np.concatenate([system, rng.integers(0, 32000, n).astype(np.int32)]) for n in own]
+    NB = sum(-(-len(p) // bs) for p in prompts) + 16
+    MB = max(-(-len(p) // bs) for p in prompts)
+
+    def admit(mgr, cached: bool):
+        hits, slots = [], []
+        for sid, p in enumerate(prompts):
+            hit = mgr.add_cached(sid, p) if cached else (mgr.add(sid) or 0)
+            sl, _ = mgr.append_tokens(sid, p[hit:])
+            hits.append(hit)
+            slots.append(sl)
+        return hits, slots
+
+    # host: admitting every request (the first computes its prompt, the rest hit the cache)
+    reps = max(1, args.steps // 5)
+    t = time.perf_counter()
+    for _ in range(reps):
+        bm = B.BlockManager(NB, 0, bs)
+        hits, _ = admit(bm, True)
+        tables_c, lens_c = bm.block_tables(list(range(S)), MB)
+        bm.close()
+    host_us = (time.perf_counter() - t) / reps / S * 1e6
+    t = time.perf_counter()
+    model = PrefixCacheModel(NB, 0, bs)
+    mhits, _ = admit(model, True)                  # the model on the same int32 token arrays
+    model_us = (time.perf_counter() - t) / S * 1e6
+    assert mhits == hits, "the library and the model disagree on the cache hits"
+    bm = B.BlockManager(NB, 0, bs)
+    admit(bm, False)
+    tables_f, lens_f = bm.block_tables(list(range(S)), MB)
+    bm.close()
+    log(f"[bench] prefix cache: {sum(h > 0 for h in hits)} of {S} requests hit, {hits[1]} tokens each; "
+        f"host {host_us:.2f} us per request (library), {model_us:.1f} us (oracle model)")
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(32)
+    kc = torch.randn((NB, H, bs, D), generator=gen, device=dev, dtype=torch.float16)
+    vc = torch.randn_like(kc)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    stream = torch.cuda.current_stream()
+    later = list(range(1, S))                       # the requests admitted after the first
+
+    def batch(tables, lens, hits_):
+        rows = [len(prompts[i]) - hits_[i] for i in later]
+        qs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+        q = torch.randn((int(qs[-1]), H, D), generator=gen, device=dev, dtype=torch.float16)
+        return (q, torch.empty_like(q), torch.from_numpy(tables[later]).to(dev), torch.from_numpy(lens[later]).to(dev),
+                torch.from_numpy(qs).to(dev), max(rows), rows)
+
+    runs = {"cached": batch(tables_c, lens_c, hits), "full": batch(tables_f, lens_f, [0] * S)}
+
+    def call(r):
+        q, out, t_dev, l_dev, qs_dev, mq, _ = runs[r]
+        B.pa_prefill(out, q, kc, vc, t_dev, l_dev, qs_dev, mq, scale, num_blocks=NB, stream=stream)
+
+    ms = {}
+    for r in runs:
+        for _ in range(args.warmup):
+            call(r)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            call(r)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms[r] = t0.elapsed_time(t1) / args.steps
+    prompt_tokens = sum(len(prompts[i]) for i in later)
+    # algorithmic flops of the cached call: each computed row attends its position + 1 tokens
+    flops = sum(sum(hits[i] + j + 1 for j in range(len(prompts[i]) - hits[i])) for i in later) * H * 4 * D
+    achieved = flops / (ms["cached"] * 1e-3) / 1e12
+    log(f"[bench] prefill of 127 admitted requests: {ms['cached'] * 1e3:.1f} us with the cache, "
+        f"{ms['full'] * 1e3:.1f} us without ({ms['full'] / ms['cached']:.1f}x)")
+    result = {
+        "metric": "prompt tokens made ready per second with automatic prefix caching (GPU prefill)",
+        "value": round(prompt_tokens / (ms["cached"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms["cached"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded token ids, K/V, q)",
+        "config": {"workload": "prefix_cache: 128 requests, 1504-token shared system prompt + 8-200 own tokens, "
+                               "32x128 MHA, fp16, block size 16; prefill of the 127 requests after the first",
+                   "parallelism": "single GPU"},
+        "prefill_us_with_cache": round(ms["cached"] * 1e3, 2),
+        "prefill_us_without_cache": round(ms["full"] * 1e3, 2),
+        "speedup": round(ms["full"] / ms["cached"], 2),
+        "prompt_tokens_from_cache": round(sum(hits[i] for i in later) / prompt_tokens, 4),
+        "host_us_per_request": round(host_us, 3),
+        "roofline": {"kernel": "prefill_kernel (the cached call)", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_call_us": round(ms["cached"] * 1e3, 3), "flops_per_call": flops},
+        "cpu_baseline": {"value": round(1e6 / model_us, 1), "unit": "requests admitted/s", "cores": 1,
+                         "kind": "oracle", "sample": "the prefix-cache model admitting the same 128 requests "
+                                                     f"({model_us:.1f} us each; the library: {host_us:.2f} us)"},
+    }
+    print(json.dumps(result), flush=True)
 
 
 def prefill_step(args):
@@ -319,6 +437,9 @@ def main():
         return
     if args.op == "prefill":
         prefill_step(args)
+        return
+    if args.op == "prefix_cache":
+        prefix_cache_step(args)
         return
     if args.op != "decode":
         block_moves(args)

@@ -394,25 +394,30 @@ class BlockManager:
         self._call("pa_bm_append", seq, n, slots, copies, 1, ctypes.byref(nc))
         return list(slots[:n]), [(copies[2 * i], copies[2 * i + 1]) for i in range(nc.value)]
 
+    @staticmethod
+    def _tokens(tokens):
+        import numpy as np
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).astype(np.int32)).reshape(-1)
+        return t, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
     def append_tokens(self, seq: int, tokens):
         """append() with the token ids given, so that the blocks they fill can be cached."""
-        tokens = [int(t) for t in tokens]
-        n = len(tokens)
-        toks = (ctypes.c_int32 * max(n, 1))(*tokens)
-        slots = (ctypes.c_int64 * max(n, 1))()
+        import numpy as np
+        keep, toks = self._tokens(tokens)
+        n = keep.size
+        slots = np.empty(max(n, 1), dtype=np.int64)
         copies = (ctypes.c_int32 * 2)()
         nc = ctypes.c_int32(0)
-        self._call("pa_bm_append_tokens", seq, toks, n, slots, copies, 1, ctypes.byref(nc))
-        return list(slots[:n]), [(copies[2 * i], copies[2 * i + 1]) for i in range(nc.value)]
+        self._call("pa_bm_append_tokens", seq, toks, n, slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                   copies, 1, ctypes.byref(nc))
+        return slots[:n].tolist(), [(copies[2 * i], copies[2 * i + 1]) for i in range(nc.value)]
 
     def add_cached(self, seq: int, prompt) -> int:
         """A new request whose table starts with the cached blocks `prompt` begins
         with; returns the prompt tokens already cached."""
-        prompt = [int(t) for t in prompt]
-        n = len(prompt)
-        toks = (ctypes.c_int32 * max(n, 1))(*prompt)
+        keep, toks = self._tokens(prompt)
         hit = ctypes.c_int32(0)
-        self._call("pa_bm_add_cached", seq, toks, n, ctypes.byref(hit))
+        self._call("pa_bm_add_cached", seq, toks, keep.size, ctypes.byref(hit))
         return hit.value
 
     def cache_stats(self):
