@@ -46,6 +46,8 @@ def parse(argv=None):
     ap.add_argument("--layout", choices=["bhtd", "bthd"], default="bhtd")
     ap.add_argument("--shared-blocks", choices=["auto", "on", "off"], default="auto",
                     help="PA_DECODE_SHARED_BLOCKS: auto = on when the workload's tables share blocks")
+    ap.add_argument("--prefix-pass", choices=["auto", "on", "off"], default="auto",
+                    help="pa_decode_shared_prefix: auto = on when the workload's tables all start with the same blocks")
     ap.add_argument("--kernel", choices=["auto", "vector", "mfma"], default="auto",
                     help="decode kernel family (pa_kernel): auto picks matrix cores for grouped-query heads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -415,6 +417,8 @@ def run_config(args, w, B):
         "dtype_code": {"f32": B.PA_F32, "f16": B.PA_F16, "bf16": B.PA_BF16}[w.dtype],
         # the caller knows when several sequences read the same blocks (a shared prefix)
         "shared": args.shared_blocks == "on" or (args.shared_blocks == "auto" and w.shared_prefix_blocks > 0),
+        # ... and can then name the prefix, read once for the whole batch
+        "prefix_pass": w.shared_prefix_blocks > 0 and (args.prefix_pass == "on" or args.prefix_pass == "auto"),
     }
 
 
@@ -481,8 +485,14 @@ def main():
             nk = torch.randn(tuple(w.new_k.shape), generator=gen, device=dev, dtype=tdt)
             nv = torch.randn(tuple(w.new_v.shape), generator=gen, device=dev, dtype=tdt)
         Ls.append((kc, vc, q, nk, nv, torch.empty_like(q)))
-    ws_bytes = B.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
-                                           w.max_blocks_per_seq, {"f32": 0, "f16": 1, "bf16": 2}[w.dtype], pt)
+    prefix_pass = cfg["prefix_pass"]
+    if prefix_pass:
+        ws_bytes = B.pa_decode_shared_prefix_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                                             w.block_size, w.max_blocks_per_seq, dtype_code,
+                                                             w.shared_prefix_blocks)
+    else:
+        ws_bytes = B.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                               w.max_blocks_per_seq, dtype_code, pt)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     kv_per_layer = w.kv_bytes()
@@ -500,15 +510,25 @@ def main():
         path_name, call_kernels = "single", f"decode_{family}_kernel"
     else:
         path_name, call_kernels = f"split-K {path_pt} tokens", f"decode_{family}_kernel + reduce_kernel"
+    if prefix_pass:
+        path_name = f"shared prefix ({w.shared_prefix_blocks} blocks) once, then split-K"
+        call_kernels = f"prefix_kernel + decode_{family}_kernel (the sequences' own blocks) + reduce_kernel"
     log(f"[bench] path: {path_name}, kernels per call: {call_kernels}")
+
+    def decode(out, q, kc, vc):
+        if prefix_pass:
+            B.pa_decode_shared_prefix(out, q, kc, vc, tables, ctx, w.scale, w.shared_prefix_blocks, layout=layout,
+                                      workspace=ws, stream=stream)
+        else:
+            B.pa_decode_ex(out, q, kc, vc, tables, ctx, w.scale, layout=layout, partition_tokens=pt,
+                           kernel=kern, shared_blocks=shared, workspace=ws, stream=stream)
 
     def step(events=None):
         for li, (kc, vc, q, nk, nv, out) in enumerate(Ls):
             B.pa_reshape_and_cache(nk, nv, kc, vc, slots, layout=layout, stream=stream)
             if events is not None:
                 events[2 * li].record(stream)
-            B.pa_decode_ex(out, q, kc, vc, tables, ctx, w.scale, layout=layout, partition_tokens=pt,
-                           kernel=kern, shared_blocks=shared, workspace=ws, stream=stream)
+            decode(out, q, kc, vc)
             if events is not None:
                 events[2 * li + 1].record(stream)
 
@@ -541,8 +561,7 @@ def main():
     d0.record(stream)
     for k in range(args.steps):
         for kc, vc, q, nk, nv, out in Ls:
-            B.pa_decode_ex(out, q, kc, vc, tables, ctx, w.scale, layout=layout, partition_tokens=pt,
-                           kernel=kern, shared_blocks=shared, workspace=ws, stream=stream)
+            decode(out, q, kc, vc)
     d1.record(stream)
     torch.cuda.synchronize()
     evented_call_ms = avg_call_ms
@@ -552,12 +571,19 @@ def main():
     # HBM bytes per call from the committed counter record, when it was taken
     # on these kernel sources (else null)
     from paged_kv_cache_405_amd import traffic as TR
-    rec = TR.lookup(args.workload, path_pt, path_kern, args.layout, shared)
+    rec = None if prefix_pass else TR.lookup(args.workload, path_pt, path_kern, args.layout, shared)
     traffic_bytes = None if rec is None else int(round(rec["bytes_per_call"]))
     traffic_source = None if rec is None else "profiles/hbm_traffic.json (rocprofv3 FETCH_SIZE, WRITE_SIZE)"
     calls = args.steps * layers
     kv_gbs = kv_per_layer * calls / (total_ms * 1e-3) / 1e9
-    achieved = kv_per_layer / (avg_call_ms * 1e-3) / 1e9
+    # the bytes a call must read: every token's K and V once -- with the prefix
+    # pass, the shared prefix once for the whole batch
+    roof_bytes = kv_per_layer
+    if prefix_pass:
+        pre = w.shared_prefix_blocks * w.block_size
+        own = np.maximum(w.context_lens.astype(np.int64) - pre, 0).sum()
+        roof_bytes = int((pre + own) * w.num_kv_heads * w.head_dim * w.k_cache.dtype.itemsize * 2)
+    achieved = roof_bytes / (avg_call_ms * 1e-3) / 1e9
     seq_layers = w.num_seqs * calls / (total_ms * 1e-3)
     result = {
         "metric": METRIC,
@@ -578,7 +604,7 @@ def main():
             "head_dim": w.head_dim, "block_size": w.block_size, "layers": layers,
             "partition_tokens": pt, "layout": args.layout, "kernel": args.kernel,
             "path": {"partition": path_name, "kernel_family": family},
-            "shared_blocks": shared, "sum_context_tokens": int(w.context_lens.sum()),
+            "shared_blocks": shared, "prefix_pass": prefix_pass, "sum_context_tokens": int(w.context_lens.sum()),
             "parallelism": "single GPU",
         },
         "seq_layers_per_s": round(seq_layers, 1),
@@ -595,7 +621,7 @@ def main():
             "traffic_source": traffic_source,
             "avg_call_us": round(avg_call_ms * 1e3, 3),
             "avg_call_us_own_events": round(evented_call_ms * 1e3, 3),
-            "bytes_per_call": kv_per_layer,
+            "bytes_per_call": roof_bytes,
         },
         "append_and_decode_us_per_layer": round(total_ms * 1e3 / calls, 3),
     }

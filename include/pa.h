@@ -237,6 +237,42 @@ pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *
                      pa_layout layout, unsigned flags, void *stream);
 
 /*
+ * pa_decode_shared_prefix -- pa_decode_ex for a batch whose block tables all
+ * start with the same prefix_blocks physical blocks (a shared system prompt;
+ * requests that point at the same blocks, "vLLM 与 PagedAttention" section
+ * 二 and "指南", "Copy-on-Write：Prefix Caching 的基础").  The same function:
+ * each sequence attends its own context_lens[s] tokens.  The prefix's K/V
+ * are read once for the whole batch -- the sequences' query rows are the
+ * columns of one matrix-core pass over them, each seeing the prefix tokens
+ * below its own context -- and each sequence's remaining blocks are read as
+ * split-K partitions; a reduce merges the two.
+ *
+ *   prefix_blocks   0 .. max_blocks_per_seq: row 0 of block_tables lists the
+ *                   prefix's blocks in its first prefix_blocks entries (those
+ *                   are the ones read, whatever context_lens[0] is); in every
+ *                   other row, the entries that are both inside the prefix
+ *                   and below the row's own block count must be the same
+ *                   blocks (a context shorter than the prefix is fine)
+ *   workspace       at least pa_decode_shared_prefix_workspace_bytes(...) bytes
+ *                   (content on entry does not matter)
+ *   other arguments as for pa_decode_ex (no kernel, partition or flags: the
+ *   prefix pass runs on the matrix cores, the rest takes the library's choice)
+ *
+ * Needs f16 or bf16, head_dim 128 or 256 and at most 16 q heads per kv head
+ * or a multiple of 16 (PA_ERR_UNSUPPORTED otherwise).  Errors as for
+ * pa_decode_ex; PA_ERR_INVALID_ARG for prefix_blocks out of range.
+ */
+pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, int prefix_blocks, float scale,
+                                  pa_dtype dtype, pa_layout layout, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+pa_status pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                                  int block_size, int max_blocks_per_seq, pa_dtype dtype,
+                                                  int prefix_blocks, size_t *bytes_out);
+
+/*
  * pa_decode_path -- the path pa_decode_ex takes for these sizes, with the
  * automatic choices resolved: *partition_out receives PA_PARTITION_SINGLE,
  * PA_PARTITION_BALANCED or the partition in tokens, *kernel_out

@@ -65,6 +65,10 @@ def lib():
             L.pa_decode.argtypes = [vp] * 6 + [i32] * 6 + [f32, i32, vp, sz, vp]
             L.pa_decode_ex.restype = i32
             L.pa_decode_ex.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, i32, i32, ctypes.c_uint32, vp, sz, vp]
+            L.pa_decode_shared_prefix.restype = i32
+            L.pa_decode_shared_prefix.argtypes = [vp] * 6 + [i32] * 8 + [f32, i32, i32, vp, sz, vp]
+            L.pa_decode_shared_prefix_workspace_bytes.restype = i32
+            L.pa_decode_shared_prefix_workspace_bytes.argtypes = [i32] * 8 + [ctypes.POINTER(sz)]
             L.pa_decode_workspace_bytes.restype = i32
             L.pa_decode_workspace_bytes.argtypes = [i32] * 8 + [ctypes.POINTER(sz)]
             L.pa_decode_path.restype = i32
@@ -222,6 +226,41 @@ def pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, *,
         None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode_ex")
+    return out
+
+
+def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                            max_blocks_per_seq, dtype_code, prefix_blocks):
+    out = ctypes.c_size_t(0)
+    st = lib().pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                       max_blocks_per_seq, dtype_code, prefix_blocks,
+                                                       ctypes.byref(out))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_shared_prefix_workspace_bytes")
+    return out.value
+
+
+def pa_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale, prefix_blocks, *,
+                            num_blocks=None, layout=PA_LAYOUT_BHTD, workspace=None, stream=None):
+    """pa_decode_ex for tables that all start with the same prefix_blocks blocks (read once for the batch)."""
+    torch = _torch()
+    code = _dtype_code(q)
+    S, Hq, D = q.shape
+    NB, bs, Hkv, D2 = cache_dims(k_cache, layout)
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, out and the caches")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    MB = block_tables.shape[1]
+    nbytes = pa_decode_shared_prefix_workspace_bytes(S, Hq, Hkv, D, bs, MB, code, int(prefix_blocks))
+    ws, ws_bytes = _workspace(q, nbytes, workspace)
+    st = lib().pa_decode_shared_prefix(
+        _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        S, Hq, Hkv, D, bs, MB, NB if num_blocks is None else int(num_blocks), int(prefix_blocks), float(scale), code,
+        int(layout), None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_shared_prefix")
     return out
 
 

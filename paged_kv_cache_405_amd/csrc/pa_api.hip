@@ -18,6 +18,8 @@
 namespace {
 
 constexpr size_t WS_ALIGN = 256;
+// split-K partition after a shared prefix, in tokens: a multiple of the block size
+#define PA_SUFFIX_TOKENS(bs) (pa::SHARED_PREFIX_SUFFIX_PARTITION / (bs) * (bs))
 
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -359,6 +361,142 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
     return pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, INT32_MAX, scale, dtype,
                         PA_LAYOUT_BHTD, PA_PARTITION_AUTO, PA_KERNEL_AUTO, 0u, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// the launch plan of a shared-prefix decode (host only; checks included)
+struct PrefixPlan {
+    Plan suffix;                  // the split-K decode over the blocks after the prefix
+    int n_chunks = 0, max_partitions = 0, prefix_group_split = 1;
+    size_t ml_bytes = 0, ws_bytes = 0;
+};
+
+pa_status make_prefix_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                           int max_blocks_per_seq, pa_dtype dtype, int prefix_blocks, PrefixPlan *pp)
+{
+    pa_status st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
+                               PA_PARTITION_SINGLE);
+    if (st != PA_OK)
+        return st;
+    if (prefix_blocks < 0 || prefix_blocks > max_blocks_per_seq)
+        return PA_ERR_INVALID_ARG;
+    const int group = num_q_heads / num_kv_heads;
+    if (!mfma_shape(dtype, head_dim, group))
+        return PA_ERR_UNSUPPORTED;
+    const int pt = PA_SUFFIX_TOKENS(block_size);
+    st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype, pt,
+                   PA_KERNEL_AUTO, &pp->suffix);
+    if (st != PA_OK)
+        return st;
+    pp->n_chunks = (prefix_blocks * block_size + pa::SHARED_PREFIX_CHUNK - 1) / pa::SHARED_PREFIX_CHUNK;
+    const int rest = max_blocks_per_seq - prefix_blocks;
+    const int pb = pt / block_size;
+    pp->max_partitions = pp->n_chunks + (rest + pb - 1) / pb;
+    pp->prefix_group_split = group <= 16 ? 1 : group / 16;
+    if ((long long)num_kv_heads * pp->prefix_group_split > 65535 || pp->max_partitions > 65535)
+        return PA_ERR_UNSUPPORTED;
+    const size_t units = (size_t)num_seqs * num_q_heads * pp->max_partitions;
+    pp->ml_bytes = round_up(units * sizeof(float2), WS_ALIGN);
+    pp->ws_bytes = pp->ml_bytes + units * (size_t)head_dim * sizeof(float);
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                                  int block_size, int max_blocks_per_seq, pa_dtype dtype,
+                                                  int prefix_blocks, size_t *bytes_out)
+{
+    if (!bytes_out)
+        return PA_ERR_INVALID_ARG;
+    PrefixPlan pp;
+    const pa_status st = make_prefix_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                          max_blocks_per_seq, dtype, prefix_blocks, &pp);
+    if (st != PA_OK)
+        return st;
+    *bytes_out = pp.ws_bytes;
+    return PA_OK;
+}
+
+pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, int prefix_blocks, float scale,
+                                  pa_dtype dtype, pa_layout layout, void *workspace, size_t workspace_bytes,
+                                  void *stream)
+{
+    if (!supported_layout(layout))
+        return PA_ERR_UNSUPPORTED;
+    if (num_blocks <= 0 || !std::isfinite(scale))
+        return PA_ERR_INVALID_ARG;
+    PrefixPlan pp;
+    pa_status st = make_prefix_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                    dtype, prefix_blocks, &pp);
+    if (st != PA_OK)
+        return st;
+    if (num_seqs == 0)
+        return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return PA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < pp.ws_bytes || !aligned(workspace, 16))
+        return PA_ERR_WORKSPACE;
+
+    pa::DecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.out = out;
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.tables = block_tables;
+    p.ctx = context_lens;
+    p.ws_ml = reinterpret_cast<float2 *>(workspace);
+    p.ws_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + pp.ml_bytes);
+    layout_strides(layout, num_kv_heads, block_size, head_dim, &p.block_stride, &p.head_stride, &p.token_stride);
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.group = num_q_heads / num_kv_heads;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    p.max_partitions = pp.max_partitions;
+    p.first_partition = pp.n_chunks;
+    p.part_base_blocks = prefix_blocks;
+    p.partition_blocks = PA_SUFFIX_TOKENS(block_size) / block_size;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    // the prefix, once for the whole batch
+    if (pp.n_chunks > 0) {
+        pa::DecodeParams px = p;
+        px.group_split = pp.prefix_group_split;
+        e = dtype == PA_F16 ? pa::launch_prefix_f16(px, head_dim, block_size, prefix_blocks * block_size, s)
+                            : pa::launch_prefix_bf16(px, head_dim, block_size, prefix_blocks * block_size, s);
+        if (e != hipSuccess)
+            return PA_ERR_HIP;
+    }
+    // each sequence's own blocks
+    if (pp.max_partitions > pp.n_chunks) {
+        pa::DecodeParams sx = p;
+        sx.group_split = pp.suffix.group_split;
+        if (pp.suffix.mfma) {
+            e = dtype == PA_F16 ? pa::launch_mfma_f16(sx, head_dim, block_size, s)
+                                : pa::launch_mfma_bf16(sx, head_dim, block_size, s);
+        } else {
+            e = dtype == PA_F16 ? pa::launch_decode_f16(sx, head_dim, block_size, pp.suffix.gt, s)
+                                : pa::launch_decode_bf16(sx, head_dim, block_size, pp.suffix.gt, s);
+        }
+        if (e != hipSuccess)
+            return PA_ERR_HIP;
+    }
+    return pa::launch_reduce(p, (int)dtype, head_dim, block_size, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_cache,

@@ -382,6 +382,56 @@ struct GqaWorker {
         t_last = limit(min(i0 + rows, nq) - 1);
     }
     int t_last;               // bind_rows: one past the last token any column attends
+
+    // shared-prefix pass of decode: column c is sequence i0 + c / gh (its
+    // query row of q [num_seqs, Hq, D]), head c % gh, and sees the tokens
+    // [c0, c1) of the prefix that every table starts with (sequence 0's table
+    // is read), below its own context.  Columns past the batch read nothing
+    // and write nothing.
+    __device__ __forceinline__ void bind_prefix(const DecodeParams &P, int hg, int i0, int c0, int c1) {
+        bind_kv(P, 0, hg, c1);
+        dup = false;
+        lo_lane = false;
+        const int rows = GQA_TILE / gh;
+        ncols = rows * gh;
+        const int i = i0 + lr / gh;
+        const bool on = lr < ncols && i < P.num_seqs;
+        load_q(static_cast<const char *>(P.q) +
+                   (((int64_t)(on ? i : i0)) * P.num_q_heads + qh0 + (on ? lr % gh : 0)) * D * ES + 8 * lg * ES,
+               on);
+        const int cap = P.max_blocks * BS;
+        int c = on ? P.ctx[i] : c1;
+        c = c < 0 ? 0 : (c > cap ? cap : c);
+        t_lo = c0;
+        t_vlim = c1;
+        t_hi = c < c1 ? c : c1;
+        int tf = t_hi;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
+            tf = min(tf, __shfl_xor(tf, off));
+        t_full = __builtin_amdgcn_readfirstlane(tf);
+        t_last = c1;
+    }
+
+    // bind_prefix columns: each (sequence, q head) leaves its (max, sum,
+    // unnormalised output) as split-K partition `part` of the workspace
+    __device__ __forceinline__ void finish_partials(const DecodeParams &P, int i0, int part) {
+        finalize();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int c = row_head(r);
+            const int i = i0 + c / gh;
+            if (!owns(r) || i >= P.num_seqs)
+                continue;
+            const int64_t sh = (int64_t)i * P.num_q_heads + qh0 + c % gh;
+            float *a = P.ws_acc + (sh * P.max_partitions + part) * D + lr;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                a[16 * t] = acc[t][r];
+            if (lr == 0)
+                P.ws_ml[sh * P.max_partitions + part] = make_float2(mrow[r], lrow[r]);
+        }
+    }
     __device__ __forceinline__ void reset() {
 #pragma unroll
         for (int t = 0; t < NT; ++t)

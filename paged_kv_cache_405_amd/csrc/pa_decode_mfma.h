@@ -26,7 +26,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     constexpr int MERGE_BYTES = NW * 16 * (D + 2) * 4;
     constexpr int LDS_TOTAL = NW * W::LDS_BYTES > MERGE_BYTES ? NW * W::LDS_BYTES : MERGE_BYTES;
 
-    const int p = blockIdx.x;
+    const int p = blockIdx.x + P.first_partition;
     const int hg = blockIdx.y;
     const int s = blockIdx.z;
 
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     const int cap = P.max_blocks * BS;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
     const int nblk = (ctx + BS - 1) / BS;
-    const int npart = nblk == 0 ? 1 : (nblk + P.partition_blocks - 1) / P.partition_blocks;
+    const int npart = num_partitions(P, nblk);
     if (p >= npart)
         return;
 
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     const int qh0 = w.qh0;
 
     // tokens [t_lo, t_hi) of this partition, covered by 16-token tiles [k0, k1)
-    const int b0 = p * P.partition_blocks;
+    const int b0 = partition_first_block(P, p);
     const int b1 = min(nblk, b0 + P.partition_blocks);
     w.t_lo = b0 * BS;
     w.t_hi = w.t_vlim = w.t_full = min(b1 * BS, ctx);
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     w.export_lds(sm_m + wave * 16, sm_l + wave * 16, sm_acc + wave * 16 * D);
     __syncthreads();
 
-    const bool single = npart == 1;
+    const bool single = npart == 1 && P.first_partition == 0;
     for (int idx = threadIdx.x; idx < gh * D; idx += NW * 64) {
         const int g = idx / D;
         const int d = idx - g * D;
@@ -100,7 +100,7 @@ constexpr int MFMA_WAVES = 4;
 template <typename T, int D, int BS>
 hipError_t launch_mfma_shape(const DecodeParams &p, hipStream_t st)
 {
-    dim3 grid(p.max_partitions, p.num_kv_heads * p.group_split, p.num_seqs);
+    dim3 grid(p.max_partitions - p.first_partition, p.num_kv_heads * p.group_split, p.num_seqs);
     if (p.kv_cached)
         hipLaunchKernelGGL((decode_mfma_kernel<T, D, BS, MFMA_WAVES, false>), grid, dim3(MFMA_WAVES * 64), 0, st, p);
     else

@@ -290,7 +290,7 @@ __global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams 
     using W = VecWorker<T, D, BS, GT, STREAM_KV>;
     constexpr int VEC = W::VEC;
 
-    const int p = blockIdx.x;
+    const int p = blockIdx.x + P.first_partition;
     const int hg = blockIdx.y;
     const int s = blockIdx.z;
 
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams 
     const int cap = P.max_blocks * BS;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
     const int nblk = (ctx + BS - 1) / BS;
-    const int npart = nblk == 0 ? 1 : (nblk + P.partition_blocks - 1) / P.partition_blocks;
+    const int npart = num_partitions(P, nblk);
     if (p >= npart)
         return;
 
@@ -314,12 +314,12 @@ __global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams 
     const int qh0 = w.qh0;
 
     // the partition's steps, taken round robin by the waves
-    const int b0 = p * P.partition_blocks;
+    const int b0 = partition_first_block(P, p);
     const int b1 = min(nblk, b0 + P.partition_blocks);
     w.run(b0 * W::NSLAB + wave, b1 * W::NSLAB, NW);
     w.merge_rows();
 
-    const bool single = npart == 1;
+    const bool single = npart == 1 && P.first_partition == 0;
     auto emit = [&](int g, int d, float M, float L, float A) {
         const int qh = qh0 + g;
         const int64_t sh = (int64_t)s * P.num_q_heads + qh;
@@ -388,8 +388,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(const DecodeParams P)
     const int cap = P.max_blocks * BS;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
     const int nblk = (ctx + BS - 1) / BS;
-    const int npart = nblk == 0 ? 1 : (nblk + P.partition_blocks - 1) / P.partition_blocks;
-    if (npart <= 1)
+    const int npart = num_partitions(P, nblk);
+    if (npart <= 1 && P.first_partition == 0)
         return;
     const int lane = threadIdx.x;
     const int64_t sh = (int64_t)s * P.num_q_heads + qh;
@@ -429,7 +429,7 @@ constexpr int DECODE_WAVES = 4;
 template <typename T, int D, int BS, int GT>
 hipError_t launch_decode_shape(const DecodeParams &p, hipStream_t st)
 {
-    dim3 grid(p.max_partitions, p.num_kv_heads * p.group_split, p.num_seqs);
+    dim3 grid(p.max_partitions - p.first_partition, p.num_kv_heads * p.group_split, p.num_seqs);
     if (p.kv_cached)
         hipLaunchKernelGGL((decode_vec_kernel<T, D, BS, GT, DECODE_WAVES, false>), grid, dim3(DECODE_WAVES * 64), 0, st, p);
     else

@@ -312,6 +312,11 @@ struct DecodeParams {
     int num_blocks;           // pool size (entries outside [0, num_blocks) contribute nothing)
     int partition_blocks;     // blocks per split-K partition
     int max_partitions;       // P (grid x extent)
+    // shared-prefix decode: partitions [0, first_partition) hold the prefix
+    // (written by the prefix pass); partition p >= first_partition covers the
+    // blocks from part_base_blocks + (p - first_partition) * partition_blocks
+    int first_partition;
+    int part_base_blocks;
     int group;                // q heads per kv head
     int group_split;          // workgroups sharing one kv head (each takes group/group_split q heads)
     float scale_log2;         // scale * log2(e)
@@ -327,6 +332,20 @@ struct DecodeParams {
     float2 *piece_ml;         // [2 * n_waves][heads per unit] (max in log2 units, sum)
     float *piece_acc;         // [2 * n_waves][heads per unit][D] unnormalised partial outputs
 };
+
+// split-K partitions of a sequence of nblk blocks, and the first block of
+// partition p (shared-prefix decode: the prefix partitions come first and
+// hold no blocks of the sequence's own; a sequence with nothing past the
+// prefix has only those)
+__device__ __forceinline__ int num_partitions(const DecodeParams &P, int nblk) {
+    if (P.first_partition == 0)
+        return nblk == 0 ? 1 : (nblk + P.partition_blocks - 1) / P.partition_blocks;
+    const int rest = nblk - P.part_base_blocks;
+    return P.first_partition + (rest > 0 ? (rest + P.partition_blocks - 1) / P.partition_blocks : 0);
+}
+__device__ __forceinline__ int partition_first_block(const DecodeParams &P, int p) {
+    return P.part_base_blocks + (p - P.first_partition) * P.partition_blocks;
+}
 
 struct AppendParams {
     const void *k;

@@ -76,6 +76,90 @@ struct PrefillTiles {
     static constexpr bool HILO = std::is_same<T, bf16_t>::value;
 };
 
+// Key tiles t_begin .. t_end - 1 of the worker's kv head, staged in pairs
+// through LDS for all the waves of the workgroup (every wave calls this with
+// the same range); the wave computes the pairs that start below my_end.
+template <typename T, int D, int BS, bool STREAM_KV>
+__device__ __forceinline__ void staged_tiles(GqaWorker<T, D, BS, STREAM_KV> &w, unsigned char PA_LDS *base, int wave,
+                                             int lane, int t_begin, int t_end, int my_end)
+{
+    using PT = PrefillTiles<T, D, BS, STREAM_KV>;
+    using W = typename PT::W;
+    constexpr int STAGES = PT::STAGES;
+    // K source rows of this lane (K loads: row i / 4, swizzled piece)
+    const int k_row = lane >> 2;
+    const int k_piece = (lane & 3) ^ ((k_row >> 1) & 3);
+    // K slot of this lane's A operand (row lane % 16, piece lane / 16)
+    const int a_row = lane & 15, a_piece = lane >> 4;
+    const int a_off = 16 * (4 * a_row + (a_piece ^ ((a_row >> 1) & 3)));
+
+    // slot st <- tiles 2 step and 2 step + 1 (a tile past the last repeats the last: same bytes, never used)
+    auto issue = [&](int step, int st) {
+        const uint32_t slot = (uint32_t)(uintptr_t)(base + st * PT::BYTES);
+#pragma unroll
+        for (int p = 0; p < PT::PER_WAVE; ++p) {
+            const int j = wave * PT::PER_WAVE + p;          // wave-uniform
+            const int h = j / PT::TILE_LOADS, jj = j % PT::TILE_LOADS;
+            const int kt = min(t_begin + 2 * step + h, t_end - 1);
+            const int2 pp = w.tile_phys(kt);
+            const bool oka = (unsigned)pp.x < (unsigned)w.num_blocks;
+            const bool okb = (unsigned)pp.y < (unsigned)w.num_blocks;
+            const int t0 = kt * GQA_TILE;
+            const uint32_t tslot = slot + h * PT::TILE_BYTES;
+            if (jj < PT::NC) {
+                // K chunk jj: this lane's row and piece
+                const bool second = BS < GQA_TILE && k_row >= BS;
+                const int64_t blk = second ? (okb ? pp.y : 0) : (oka ? pp.x : 0);
+                const int in_row = BS < GQA_TILE ? (k_row & (BS - 1)) : (t0 % BS) + k_row;
+                const char *src = w.kpool + blk * w.blk_bytes + (int64_t)in_row * w.tok_bytes + 64 * jj + 16 * k_piece;
+                load_lds_asm<STREAM_KV>(src, tslot + jj * 1024);
+            } else {
+                // V load i, as the worker lays V out: token 4 grp + lane % 4, chunk lane / 4
+                const int i = jj - PT::NC;
+                const int grp = i / (D / 128), half = i % (D / 128);
+                const bool second = BS < GQA_TILE && 4 * grp >= BS;
+                const int64_t blk = second ? (okb ? pp.y : 0) : (oka ? pp.x : 0);
+                const int in_row = BS < GQA_TILE ? (4 * grp) & (BS - 1) : (t0 % BS) + 4 * grp;
+                const char *src = w.vpool + blk * w.blk_bytes + (int64_t)in_row * w.tok_bytes + 256 * half + w.v_src;
+                load_lds_asm<STREAM_KV>(src, tslot + PT::K_BYTES + i * W::LOAD_LDS);
+            }
+        }
+    };
+    // the wave's view of tile kt in slot st: K fragments from LDS, V in place; a
+    // tile past the last is unmapped (masked out)
+    auto view = [&](int kt, const unsigned char PA_LDS *ts, typename W::Buf &b) {
+#pragma unroll
+        for (int c = 0; c < PT::NC; ++c)
+            b.k[c] = *reinterpret_cast<const gqa_u32x4 PA_LDS *>(ts + c * 1024 + a_off);
+        b.v = const_cast<unsigned char PA_LDS *>(ts + PT::K_BYTES);
+        const int2 pp = kt < t_end ? w.tile_phys(kt) : make_int2(-1, -1);
+        b.oka = (unsigned)pp.x < (unsigned)w.num_blocks;
+        b.okb = (unsigned)pp.y < (unsigned)w.num_blocks;
+    };
+
+    const int n_steps = (t_end - t_begin + 1) / 2;
+    if (n_steps > 0) {
+#pragma unroll
+        for (int i = 0; i < STAGES - 1; ++i)
+            issue(min(i, n_steps - 1), i);
+        for (int step = 0; step < n_steps; ++step) {
+            vm_wait<PT::PER_WAVE * (STAGES - 2)>();        // this wave's loads of this step's slot
+            asm volatile("s_barrier" ::: "memory");       // the slot complete; the one before done by all
+            issue(min(step + STAGES - 1, n_steps - 1), (step + STAGES - 1) % STAGES);
+            const int kt = t_begin + 2 * step;
+            if (kt < my_end) {
+                const unsigned char PA_LDS *ss = base + (step % STAGES) * PT::BYTES;
+                typename W::Buf b0, b1;
+                view(kt, ss, b0);
+                view(kt + 1, ss + PT::TILE_BYTES, b1);
+                w.template compute_pair<PT::HILO>(kt, b0, b1);
+            }
+        }
+        // every load into LDS has landed before the workgroup ends
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+}
+
 template <typename T, int D, int BS, bool STREAM_KV>
 __global__ __launch_bounds__(PF_WAVES * 64) void prefill_kernel(const DecodeParams P, int col_groups, int total_wg)
 {
@@ -122,79 +206,8 @@ __global__ __launch_bounds__(PF_WAVES * 64) void prefill_kernel(const DecodePara
     const int n_tiles = (t_end + GQA_TILE - 1) / GQA_TILE;
     const int my_tiles = active ? (w.t_last + GQA_TILE - 1) / GQA_TILE : 0;
 
-    unsigned char PA_LDS *base = (unsigned char PA_LDS *)lds;
-    // K source rows of this lane (K loads: row i / 4, swizzled piece)
-    const int k_row = lane >> 2;
-    const int k_piece = (lane & 3) ^ ((k_row >> 1) & 3);
-    // K slot of this lane's A operand (row lane % 16, piece lane / 16)
-    const int a_row = lane & 15, a_piece = lane >> 4;
-    const int a_off = 16 * (4 * a_row + (a_piece ^ ((a_row >> 1) & 3)));
-
-    // slot st <- tiles 2 step and 2 step + 1 (a tile past the last repeats the last: same bytes, never used)
-    auto issue = [&](int step, int st) {
-        const uint32_t slot = (uint32_t)(uintptr_t)(base + st * PT::BYTES);
-#pragma unroll
-        for (int p = 0; p < PT::PER_WAVE; ++p) {
-            const int j = wave * PT::PER_WAVE + p;          // wave-uniform
-            const int h = j / PT::TILE_LOADS, jj = j % PT::TILE_LOADS;
-            const int kt = min(2 * step + h, n_tiles - 1);
-            const int2 pp = w.tile_phys(kt);
-            const bool oka = (unsigned)pp.x < (unsigned)w.num_blocks;
-            const bool okb = (unsigned)pp.y < (unsigned)w.num_blocks;
-            const int t0 = kt * GQA_TILE;
-            const uint32_t tslot = slot + h * PT::TILE_BYTES;
-            if (jj < PT::NC) {
-                // K chunk jj: this lane's row and piece
-                const bool second = BS < GQA_TILE && k_row >= BS;
-                const int64_t blk = second ? (okb ? pp.y : 0) : (oka ? pp.x : 0);
-                const int in_row = BS < GQA_TILE ? (k_row & (BS - 1)) : (t0 % BS) + k_row;
-                const char *src = w.kpool + blk * w.blk_bytes + (int64_t)in_row * w.tok_bytes + 64 * jj + 16 * k_piece;
-                load_lds_asm<STREAM_KV>(src, tslot + jj * 1024);
-            } else {
-                // V load i, as the worker lays V out: token 4 grp + lane % 4, chunk lane / 4
-                const int i = jj - PT::NC;
-                const int grp = i / (D / 128), half = i % (D / 128);
-                const bool second = BS < GQA_TILE && 4 * grp >= BS;
-                const int64_t blk = second ? (okb ? pp.y : 0) : (oka ? pp.x : 0);
-                const int in_row = BS < GQA_TILE ? (4 * grp) & (BS - 1) : (t0 % BS) + 4 * grp;
-                const char *src = w.vpool + blk * w.blk_bytes + (int64_t)in_row * w.tok_bytes + 256 * half + w.v_src;
-                load_lds_asm<STREAM_KV>(src, tslot + PT::K_BYTES + i * W::LOAD_LDS);
-            }
-        }
-    };
-    // the wave's view of tile kt in slot st: K fragments from LDS, V in place; a
-    // tile past the last is unmapped (masked out)
-    auto view = [&](int kt, const unsigned char PA_LDS *ts, typename W::Buf &b) {
-#pragma unroll
-        for (int c = 0; c < PT::NC; ++c)
-            b.k[c] = *reinterpret_cast<const gqa_u32x4 PA_LDS *>(ts + c * 1024 + a_off);
-        b.v = const_cast<unsigned char PA_LDS *>(ts + PT::K_BYTES);
-        const int2 pp = kt < n_tiles ? w.tile_phys(kt) : make_int2(-1, -1);
-        b.oka = (unsigned)pp.x < (unsigned)w.num_blocks;
-        b.okb = (unsigned)pp.y < (unsigned)w.num_blocks;
-    };
-
     w.reset();
-    const int n_steps = (n_tiles + 1) / 2;
-    if (n_steps > 0) {
-#pragma unroll
-        for (int i = 0; i < STAGES - 1; ++i)
-            issue(min(i, n_steps - 1), i);
-        for (int step = 0; step < n_steps; ++step) {
-            vm_wait<PT::PER_WAVE * (STAGES - 2)>();        // this wave's loads of this step's slot
-            asm volatile("s_barrier" ::: "memory");       // the slot complete; the one before done by all
-            issue(min(step + STAGES - 1, n_steps - 1), (step + STAGES - 1) % STAGES);
-            if (2 * step < my_tiles) {
-                const unsigned char PA_LDS *ss = base + (step % STAGES) * PT::BYTES;
-                typename W::Buf b0, b1;
-                view(2 * step, ss, b0);
-                view(2 * step + 1, ss + PT::TILE_BYTES, b1);
-                w.template compute_pair<PT::HILO>(2 * step, b0, b1);
-            }
-        }
-        // every load into LDS has landed before the workgroup ends
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    staged_tiles<T, D, BS, STREAM_KV>(w, (unsigned char PA_LDS *)lds, wave, lane, 0, n_tiles, my_tiles);
     if (active)
         w.finish_rows(P, q_first, i0, nq);
 }
@@ -214,6 +227,90 @@ hipError_t launch_prefill_shape(const DecodeParams &p, int max_query_len, hipStr
     hipLaunchKernelGGL((prefill_kernel<T, D, BS, false>), grid, dim3(PF_WAVES * 64), 0, st, p, col_groups,
                        (int)total);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Shared-prefix decode, first pass.  When every table of a decode batch
+// starts with the same blocks (a common system prompt, copy-on-write sharing:
+// "vLLM 与 PagedAttention" section 二, "指南" "Copy-on-Write：Prefix Caching
+// 的基础"), those blocks' K/V need to be read once, not once per sequence:
+// the batch's query rows are the columns of one pass over them, like a
+// prefill's rows but with no causal order -- each sequence sees the prefix
+// tokens below its own context.  The prefix is cut into chunks of PX_CHUNK
+// tokens, one workgroup per (group of PF_WAVES column tiles, chunk, head
+// group); each (sequence, q head) leaves the chunk's (max, sum, unnormalised
+// output) as split-K partition `chunk`.  The decode kernels then take the
+// sequences' own blocks as the partitions after these, and the split-K reduce
+// merges them all.
+constexpr int PX_CHUNK = 128;   // prefix tokens per chunk (a multiple of two tiles; SHARED_PREFIX_CHUNK)
+
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(PF_WAVES * 64) void prefix_kernel(const DecodeParams P, int col_groups, int n_chunks,
+                                                               int prefix_tokens, int total_wg)
+{
+    static_assert(D % 128 == 0, "the matrix-core worker needs head_dim 128 or 256");
+    using PT = PrefillTiles<T, D, BS, false>;
+    using W = typename PT::W;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[PT::STAGES * PT::BYTES];
+
+    // XCD-major, column groups fastest: the groups reading one chunk of one kv head share an L2
+    const int per_xcd = (total_wg + 7) / 8;
+    const int lg_id = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (lg_id >= total_wg)
+        return;
+    const int cg = lg_id % col_groups;
+    const int c = (lg_id / col_groups) % n_chunks;
+    const int hg = lg_id / col_groups / n_chunks;
+    const int gh = P.group / P.group_split;
+    const int rows = GQA_TILE / gh;
+    const int i0g = cg * PF_WAVES * rows;                // first sequence of the group (inside the batch)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i0 = i0g + wave * rows;
+    const bool active = i0 < P.num_seqs;
+    const int c0 = c * PX_CHUNK;
+    const int c1 = min(prefix_tokens, c0 + PX_CHUNK);
+    W w;
+    w.init_lane(lane);
+    w.bind_prefix(P, hg, active ? i0 : i0g, c0, c1);
+    w.reset();
+    const int t_end = (c1 + GQA_TILE - 1) / GQA_TILE;
+    staged_tiles<T, D, BS, false>(w, (unsigned char PA_LDS *)lds, wave, lane, c0 / GQA_TILE, t_end,
+                                  active ? t_end : 0);
+    if (active)
+        w.finish_partials(P, i0, c);
+}
+
+template <typename T, int D, int BS>
+hipError_t launch_prefix_shape(const DecodeParams &p, int prefix_tokens, hipStream_t st)
+{
+    const int rows = GQA_TILE / (p.group / p.group_split);
+    const int col_tiles = (p.num_seqs + rows - 1) / rows;
+    const int col_groups = (col_tiles + PF_WAVES - 1) / PF_WAVES;
+    const int n_chunks = (prefix_tokens + PX_CHUNK - 1) / PX_CHUNK;
+    if (n_chunks != p.first_partition)
+        return hipErrorInvalidValue;
+    const long long total = (long long)col_groups * n_chunks * p.num_kv_heads * p.group_split;
+    if (total > (1LL << 30))
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((total + 7) / 8 * 8));
+    hipLaunchKernelGGL((prefix_kernel<T, D, BS>), grid, dim3(PF_WAVES * 64), 0, st, p, col_groups, n_chunks,
+                       prefix_tokens, (int)total);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_prefix_dtype(const DecodeParams &p, int head_dim, int bs, int prefix_tokens, hipStream_t st)
+{
+    switch (head_dim * 64 + bs) {
+    case 128 * 64 + 8: return launch_prefix_shape<T, 128, 8>(p, prefix_tokens, st);
+    case 128 * 64 + 16: return launch_prefix_shape<T, 128, 16>(p, prefix_tokens, st);
+    case 128 * 64 + 32: return launch_prefix_shape<T, 128, 32>(p, prefix_tokens, st);
+    case 256 * 64 + 8: return launch_prefix_shape<T, 256, 8>(p, prefix_tokens, st);
+    case 256 * 64 + 16: return launch_prefix_shape<T, 256, 16>(p, prefix_tokens, st);
+    case 256 * 64 + 32: return launch_prefix_shape<T, 256, 32>(p, prefix_tokens, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <typename T, int D>

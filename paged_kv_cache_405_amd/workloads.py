@@ -256,8 +256,9 @@ def llama70b_gqa(seed: int = 5, poison: bool = True, append: bool = True, num_se
 def custom(name: str, dtype: str, ctxs, num_q_heads: int, num_kv_heads: int, head_dim: int,
            block_size: int, seed: int = 0, poison: bool = True, append: bool = False,
            free_fraction: float = 0.10, table_pad: int = 0, scale: Optional[float] = None,
-           partition_tokens: int = 0) -> Workload:
-    """Any shape, for edge cases: explicit context lengths, optional extra table columns."""
+           partition_tokens: int = 0, shared_prefix_blocks: int = 0) -> Workload:
+    """Any shape, for edge cases: explicit context lengths, optional extra table columns; with
+    shared_prefix_blocks every table starts with the same blocks (as far as its own blocks go)."""
     rng = np.random.default_rng(seed)
     ctx = np.asarray(ctxs, dtype=np.int32)
     nblk = [blocks_needed(c, block_size) for c in ctx]
@@ -269,7 +270,7 @@ def custom(name: str, dtype: str, ctxs, num_q_heads: int, num_kv_heads: int, hea
     w = _finish(name, dtype, rng, (len(ctx), num_q_heads, head_dim), ctx, block_size, num_kv_heads,
                 head_dim, MB, poison, append,
                 scale if scale is not None else 1.0 / math.sqrt(head_dim), partition_tokens,
-                f"custom {name}", NB=NB)
+                f"custom {name}", NB=NB, shared_prefix_blocks=shared_prefix_blocks or None)
     return w
 
 

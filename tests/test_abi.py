@@ -254,3 +254,38 @@ def _prefill(**kw):
 ])
 def test_prefill_checks_arguments_first(kw, status):
     assert _prefill(**kw) == status
+
+
+def _shared(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, S=2, Hq=8, Hkv=2, D=128, bs=16, MB=8, NB=32, P=3,
+             scale=0.125, dt=B.PA_F16, layout=B.PA_LAYOUT_BHTD, ws=None, wsb=0)
+    a.update(kw)
+    return B.lib().pa_decode_shared_prefix(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["Hq"],
+                                           a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["P"], a["scale"], a["dt"],
+                                           a["layout"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=0), B.PA_OK),
+    (dict(P=-1), B.PA_ERR_INVALID_ARG), (dict(P=9), B.PA_ERR_INVALID_ARG),
+    (dict(dt=B.PA_F32), B.PA_ERR_UNSUPPORTED), (dict(D=64), B.PA_ERR_UNSUPPORTED),
+    (dict(Hq=40, Hkv=2), B.PA_ERR_UNSUPPORTED), (dict(layout=7), B.PA_ERR_UNSUPPORTED),
+    (dict(q=None), B.PA_ERR_INVALID_ARG), (dict(out=FAKE + 4), B.PA_ERR_INVALID_ARG),
+    (dict(NB=0), B.PA_ERR_INVALID_ARG), (dict(scale=float("nan")), B.PA_ERR_INVALID_ARG),
+    (dict(), B.PA_ERR_WORKSPACE),
+])
+def test_shared_prefix_checks_arguments_first(kw, status):
+    # every check runs before anything touches the device
+    assert _shared(**kw) == status
+
+
+def test_shared_prefix_workspace_query():
+    sz = ctypes.c_size_t(0)
+    L = B.lib()
+    assert L.pa_decode_shared_prefix_workspace_bytes(4, 8, 2, 128, 16, 10, B.PA_F16, 4, ctypes.byref(sz)) == B.PA_OK
+    # 4 prefix tokens chunks of 128 (64 tokens: 1 chunk) + ceil(6 * 16 / 512) = 1 suffix partition, per (seq, head)
+    units = 4 * 8 * 2
+    assert sz.value >= units * (8 + 128 * 4)
+    assert L.pa_decode_shared_prefix_workspace_bytes(4, 8, 2, 128, 16, 10, B.PA_F16, 11, ctypes.byref(sz)) == \
+        B.PA_ERR_INVALID_ARG
+    assert L.pa_decode_shared_prefix_workspace_bytes(4, 8, 2, 128, 16, 10, B.PA_F16, 4, None) == B.PA_ERR_INVALID_ARG
