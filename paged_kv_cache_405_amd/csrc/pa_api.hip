@@ -41,6 +41,12 @@ bool mfma_shape(pa_dtype dtype, int head_dim, int group)
 // below it the per-token vector work is small enough for the VALU.
 constexpr int MFMA_MIN_GROUP = 4;
 constexpr long long AUTO_UNITS_PER_CU = 4;   // single pass at or above this many units per compute unit
+// grid kernels take sequences longest first (seq_of_row) when a unit can
+// hold more than this many tokens; below it the ranking costs more than the
+// tail it saves (measured on MI355X: the shared-prefix call, whose suffix
+// pass has units of at most 208 tokens, 73.2 us with the ranking against
+// 69.2 us without)
+constexpr long long ORDER_ROWS_MIN_TOKENS = 512;
 
 struct Plan {
     bool mfma = false;          // grouped-query matrix-core kernel
@@ -292,6 +298,7 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
     p.tables = block_tables;
     p.ctx = context_lens;
     p.kv_cached = (flags & PA_DECODE_SHARED_BLOCKS) ? 1 : 0;
+    p.order_rows = (int64_t)max_blocks_per_seq * block_size > ORDER_ROWS_MIN_TOKENS ? 1 : 0;
     if (pl.stream) {
         char *ws = static_cast<char *>(workspace);
         p.n_waves = pl.n_waves;
@@ -470,6 +477,7 @@ pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
     p.max_partitions = pp.max_partitions;
     p.first_partition = pp.n_chunks;
     p.part_base_blocks = prefix_blocks;
+    p.order_rows = (int64_t)(max_blocks_per_seq - prefix_blocks) * block_size > ORDER_ROWS_MIN_TOKENS ? 1 : 0;
     p.partition_blocks = PA_SUFFIX_TOKENS(block_size) / block_size;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;

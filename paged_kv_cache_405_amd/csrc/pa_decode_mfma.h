@@ -28,11 +28,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
 
     const int p = blockIdx.x + P.first_partition;
     const int hg = blockIdx.y;
-    const int s = blockIdx.z;
-
-    int ctx = P.ctx[s];
-    const int cap = P.max_blocks * BS;
-    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    int ctx;
+    const int s = seq_of_row(P, blockIdx.z, BS, ctx);
     const int nblk = (ctx + BS - 1) / BS;
     const int npart = num_partitions(P, nblk);
     if (p >= npart)

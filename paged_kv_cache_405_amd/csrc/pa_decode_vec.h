@@ -36,6 +36,12 @@ namespace pa {
 #ifndef PA_VEC_STAGES
 #define PA_VEC_STAGES 2         // steps in the register pipeline of the vector kernel
 #endif
+#ifndef PA_VEC_NLD
+#define PA_VEC_NLD 2            // most wave-wide loads of K (and of V) per step
+#endif
+#ifndef PA_VEC_WAVES_PER_EU
+#define PA_VEC_WAVES_PER_EU 1   // occupancy floor handed to the register allocator
+#endif
 
 // One wave's share of the work on one (sequence, kv head): the online-softmax
 // state of GT query heads and the step pipeline that feeds it.  A step is a
@@ -55,7 +61,7 @@ struct VecWorker {
     static constexpr int ROWS = TPL < BS ? TPL : BS; // rows that carry tokens
     static constexpr bool ALL_ROWS = TPL <= BS;
     static constexpr int NLD_TILE = BS / ROWS;       // wave-wide loads per (block, kv head) tile
-    static constexpr int NLD = NLD_TILE < 4 ? NLD_TILE : 4;   // loads per step (a slab of the tile)
+    static constexpr int NLD = NLD_TILE < PA_VEC_NLD ? NLD_TILE : PA_VEC_NLD;   // loads per step (a slab of the tile)
     static constexpr int NSLAB = NLD_TILE / NLD;     // steps per tile
     static constexpr int SLAB_TOK = NLD * ROWS;      // tokens per step
 
@@ -285,18 +291,16 @@ struct VecWorker {
 };
 
 template <typename T, int D, int BS, int GT, int NW, bool STREAM_KV>
-__global__ __launch_bounds__(NW * 64) void decode_vec_kernel(const DecodeParams P)
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_VEC_WAVES_PER_EU)))
+void decode_vec_kernel(const DecodeParams P)
 {
     using W = VecWorker<T, D, BS, GT, STREAM_KV>;
     constexpr int VEC = W::VEC;
 
     const int p = blockIdx.x + P.first_partition;
     const int hg = blockIdx.y;
-    const int s = blockIdx.z;
-
-    int ctx = P.ctx[s];
-    const int cap = P.max_blocks * BS;
-    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    int ctx;
+    const int s = seq_of_row(P, blockIdx.z, BS, ctx);
     const int nblk = (ctx + BS - 1) / BS;
     const int npart = num_partitions(P, nblk);
     if (p >= npart)
