@@ -317,10 +317,12 @@ void decode_vec_kernel(const DecodeParams P)
     const int chunk = w.chunk;
     const int qh0 = w.qh0;
 
-    // the partition's steps, taken round robin by the waves
+    // the partition's steps, taken round robin by the waves; a step past
+    // the last context token is not read (the last block may be partly full)
     const int b0 = partition_first_block(P, p);
     const int b1 = min(nblk, b0 + P.partition_blocks);
-    w.run(b0 * W::NSLAB + wave, b1 * W::NSLAB, NW);
+    const int q_end = (min(ctx, b1 * BS) + W::SLAB_TOK - 1) / W::SLAB_TOK;
+    w.run(b0 * W::NSLAB + wave, q_end, NW);
     w.merge_rows();
 
     const bool single = npart == 1 && P.first_partition == 0;
@@ -428,7 +430,10 @@ __global__ __launch_bounds__(64) void reduce_kernel(const DecodeParams P)
 // ---------------------------------------------------------------------------
 // host-side dispatch over the compile-time shape
 // ---------------------------------------------------------------------------
-constexpr int DECODE_WAVES = 4;
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+constexpr int DECODE_WAVES = PA_DECODE_WAVES;
 
 template <typename T, int D, int BS, int GT>
 hipError_t launch_decode_shape(const DecodeParams &p, hipStream_t st)

@@ -38,7 +38,10 @@ hipError_t launch_prefill_f16(const DecodeParams &p, int head_dim, int block_siz
 hipError_t launch_prefill_bf16(const DecodeParams &p, int head_dim, int block_size, int max_query_len, hipStream_t st);
 // shared-prefix decode, first pass: the prefix's split-K partitions 0 .. first_partition - 1,
 // one per SHARED_PREFIX_CHUNK tokens of the prefix (the kernel's chunk)
-constexpr int SHARED_PREFIX_CHUNK = 128;
+#ifndef PA_PREFIX_CHUNK
+#define PA_PREFIX_CHUNK 256
+#endif
+constexpr int SHARED_PREFIX_CHUNK = PA_PREFIX_CHUNK;
 constexpr int SHARED_PREFIX_SUFFIX_PARTITION = 512;   // tokens per split-K partition after the prefix
 hipError_t launch_prefix_f16(const DecodeParams &p, int head_dim, int block_size, int prefix_tokens, hipStream_t st);
 hipError_t launch_prefix_bf16(const DecodeParams &p, int head_dim, int block_size, int prefix_tokens, hipStream_t st);

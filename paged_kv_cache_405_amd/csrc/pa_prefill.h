@@ -242,7 +242,10 @@ hipError_t launch_prefill_shape(const DecodeParams &p, int max_query_len, hipStr
 // output) as split-K partition `chunk`.  The decode kernels then take the
 // sequences' own blocks as the partitions after these, and the split-K reduce
 // merges them all.
-constexpr int PX_CHUNK = 128;   // prefix tokens per chunk (a multiple of two tiles; SHARED_PREFIX_CHUNK)
+#ifndef PA_PREFIX_CHUNK
+#define PA_PREFIX_CHUNK 256
+#endif
+constexpr int PX_CHUNK = PA_PREFIX_CHUNK;   // prefix tokens per chunk (a multiple of two tiles; SHARED_PREFIX_CHUNK)
 
 template <typename T, int D, int BS>
 __global__ __launch_bounds__(PF_WAVES * 64) void prefix_kernel(const DecodeParams P, int col_groups, int n_chunks,

@@ -283,7 +283,7 @@ def test_shared_prefix_workspace_query():
     sz = ctypes.c_size_t(0)
     L = B.lib()
     assert L.pa_decode_shared_prefix_workspace_bytes(4, 8, 2, 128, 16, 10, B.PA_F16, 4, ctypes.byref(sz)) == B.PA_OK
-    # 4 prefix tokens chunks of 128 (64 tokens: 1 chunk) + ceil(6 * 16 / 512) = 1 suffix partition, per (seq, head)
+    # 4 prefix blocks in chunks of 256 tokens (64 tokens: 1 chunk) + ceil(6 * 16 / 512) = 1 suffix partition, per (seq, head)
     units = 4 * 8 * 2
     assert sz.value >= units * (8 + 128 * 4)
     assert L.pa_decode_shared_prefix_workspace_bytes(4, 8, 2, 128, 16, 10, B.PA_F16, 11, ctypes.byref(sz)) == \

@@ -1,7 +1,8 @@
 """GPU parity of the shared-prefix decode (pa_decode_shared_prefix) with the
 fp64 oracle's plain paged decode of every sequence over its own table: the
 shared-prefix workload (128 sequences, 94 shared blocks), and edge cases --
-prefixes of 1 to 6 blocks, contexts shorter than, equal to and longer than
+prefixes of 1 to 20 blocks (one to three prefix chunks, the last one
+partial), contexts shorter than, equal to and longer than
 the prefix, an empty context, every block size, both head dims and dtypes,
 grouped-query ratios up to 32 -- and the plain decode path agrees too."""
 import numpy as np
@@ -46,7 +47,7 @@ def _cases():
 
 
 @pytest.mark.parametrize("dtype,D,bs,Hq,Hkv", _cases())
-@pytest.mark.parametrize("P", [1, 3, 6])
+@pytest.mark.parametrize("P", [1, 3, 6, 20])
 def test_edges(dtype, D, bs, Hq, Hkv, P):
     pt = P * bs
     # row 0 holds the whole prefix; the others: shorter, equal, longer, empty, one token
