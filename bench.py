@@ -39,7 +39,8 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "llama70b_gqa", "mixed_bs8", "mixed_bs16", "mixed_bs32", "shared_prefix"])
+                    choices=["llama7b", "llama70b_gqa", "llama70b_tp8", "mixed_bs8", "mixed_bs16", "mixed_bs32",
+                             "shared_prefix"])
     ap.add_argument("--layers", type=int, default=None, help="default: 32 (7B-shaped), 80 (70B-shaped)")
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="0 = library's choice (default), -1 = single pass, -2 = balanced schedule, N = split-K partition of N tokens")
@@ -409,7 +410,7 @@ def cpu_baseline(w, target_s):
 def run_config(args, w, B):
     """The host-side settings of a run (no device needed)."""
     return {
-        "layers": args.layers or (80 if w.num_q_heads == 64 else 32),
+        "layers": args.layers or (80 if w.name.startswith("llama70b") else 32),
         "layout": B.PA_LAYOUT_BHTD if args.layout == "bhtd" else B.PA_LAYOUT_BTHD,
         # the library's own choice unless a partition is asked for
         "pt": B.PA_PARTITION_AUTO if args.partition_tokens is None else args.partition_tokens,

@@ -219,9 +219,14 @@ void decode_stream_kernel(const DecodeParams P)
 // Merge the pieces of every unit the stream kernel cut: one wave per (unit,
 // head of the unit), grid x = sequence, y = head group, z = head.  The piece
 // list is known from its two ends, so no load waits on another: first the
-// reference max over the pieces (lanes over pieces), then the rescaled sums
-// (lanes over dims).
-constexpr int FEW_PIECES = 16;   // pieces per unit the reduce merges in one batch of loads
+// reference max over the pieces (lanes over pieces), then the weights (lane i
+// weighs piece i of a round of 64) and the rescaled sums over the round's
+// pieces in batches of FEW_PIECES, each batch's loads all in flight at once
+// (lanes over dims).  Pieces are added in order, so results are
+// bit-reproducible.  A unit of a small batch can be cut over many waves (32
+// sequences of one kv head over 1024 waves: about 33 pieces each); with one
+// load in flight per piece its merge took 32 us, batched it takes a few.
+constexpr int FEW_PIECES = 16;   // pieces whose loads the reduce issues in one batch
 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void stream_reduce_kernel(const DecodeParams P, int heads_per_unit)
@@ -249,60 +254,49 @@ __global__ __launch_bounds__(64) void stream_reduce_kernel(const DecodeParams P,
 #pragma unroll
     for (int e = 0; e < E; ++e)
         A[e] = 0.f;
-    float L = 0.f;
     const int np = w1 - w0 + 1;
-    if (every_wave && np <= FEW_PIECES) {
-        // the usual case: every load of the merge goes out at once -- each
-        // lane's (max, sum) of piece `lane` and the outputs of all pieces
-        const float2 ml = lane < np ? P.piece_ml[slot(w0 + lane)] : make_float2(NEG_BIG, 0.f);
-        float a[FEW_PIECES][E];
-#pragma unroll
-        for (int i = 0; i < FEW_PIECES; ++i)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                a[i][e] = i < np && lane + 64 * e < D ? P.piece_acc[slot(w0 + i) * D + lane + 64 * e] : 0.f;
-        const float M = group_max<64>(ml.x);
-        const float c = fast_exp2(ml.x - M);
-        L = group_sum<64>(ml.y * c);
-#pragma unroll
-        for (int i = 0; i < FEW_PIECES; ++i) {
-            const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), i));
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                A[e] = fmaf(a[i][e], ci, A[e]);   // pieces past np hold 0
+
+    // the reference max: one piece per lane, 64 at a time
+    float M = NEG_BIG;
+    for (int w = w0 + lane; w <= w1; w += 64)
+        if (!empty(w))
+            M = fmaxf(M, P.piece_ml[slot(w)].x);
+    M = group_max<64>(M);
+
+    float L = 0.f;
+    for (int r0 = 0; r0 < np; r0 += 64) {
+        // lane i weighs piece r0 + i (an empty range left no piece: weight 0)
+        const int wl = w0 + r0 + lane;
+        float c = 0.f;
+        if (r0 + lane < np && !empty(wl)) {
+            const float2 ml = P.piece_ml[slot(wl)];
+            c = fast_exp2(ml.x - M);
+            L = fmaf(ml.y, c, L);
         }
-    } else {
-        // the reference max: one piece per lane, 64 at a time
-        float M = NEG_BIG;
-        for (int w = w0 + lane; w <= w1; w += 64)
-            if (!empty(w))
-                M = fmaxf(M, P.piece_ml[slot(w)].x);
-        M = group_max<64>(M);
-        // each lane weighs one piece of a round of 64, then the wave adds the
-        // round's outputs dim by dim with those weights
-        for (int base = w0; base <= w1; base += 64) {
-            const int w = base + lane;
-            float c = 0.f;
-            if (w <= w1 && !empty(w)) {
-                const float2 ml = P.piece_ml[slot(w)];
-                c = fast_exp2(ml.x - M);
-                L = fmaf(ml.y, c, L);
-            }
-            const int cnt = min(64, w1 - base + 1);
-#pragma unroll 4
-            for (int i = 0; i < cnt; ++i) {
-                if (empty(base + i))
-                    continue;
-                const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), i));
-                const float *a = P.piece_acc + slot(base + i) * D;
+        const int cnt = min(64, np - r0);
+        for (int b0 = 0; b0 < cnt; b0 += FEW_PIECES) {
+            // every load of the batch first; a piece past the end or of an
+            // empty range is selected out, never multiplied by its weight
+            float a[FEW_PIECES][E];
+#pragma unroll
+            for (int i = 0; i < FEW_PIECES; ++i) {
+                const int w = w0 + r0 + b0 + i;
+                const bool ok = b0 + i < cnt && !empty(w);
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    if (lane + 64 * e < D)
-                        A[e] = fmaf(a[lane + 64 * e], ci, A[e]);
+                    a[i][e] = ok && lane + 64 * e < D ? P.piece_acc[slot(w) * D + lane + 64 * e] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < FEW_PIECES; ++i) {
+                const int k = min(b0 + i, 63);
+                const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), k));
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    A[e] = fmaf(a[i][e], ci, A[e]);   // pieces past the end hold 0
             }
         }
-        L = group_sum<64>(L);
     }
+    L = group_sum<64>(L);
     const int kvh = hg / P.group_split;
     const int qh = kvh * P.group + (hg - kvh * P.group_split) * heads_per_unit + g;
     const int64_t o = ((int64_t)s * P.num_q_heads + qh) * D;

@@ -253,6 +253,20 @@ def llama70b_gqa(seed: int = 5, poison: bool = True, append: bool = True, num_se
                    f"{num_seqs} seqs, 64 q / 8 kv heads x 128, bf16, bs 16, ctx U[{min_ctx},{max_ctx}]")
 
 
+def llama70b_tp8(seed: int = 5, poison: bool = True, append: bool = True, num_seqs: int = 32,
+                 min_ctx: int = 2048, max_ctx: int = 8192) -> Workload:
+    """One GPU's share of the Llama-2-70B-shaped workload when its heads are split over
+    8 GPUs: 8 q heads over 1 kv head x 128, bf16, block size 16, the same context
+    lengths (same seed, U[2048, 8192])."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(min_ctx, max_ctx + 1, size=num_seqs)
+    MB = blocks_needed(max_ctx, 16)
+    return _finish("llama70b_tp8", "bf16", rng, (num_seqs, 8, 128), ctx, 16, 1, 128, MB, poison, append,
+                   1.0 / math.sqrt(128), 512,
+                   f"{num_seqs} seqs, 8 q / 1 kv head x 128 (one of 8 head shards), bf16, bs 16, "
+                   f"ctx U[{min_ctx},{max_ctx}]")
+
+
 def custom(name: str, dtype: str, ctxs, num_q_heads: int, num_kv_heads: int, head_dim: int,
            block_size: int, seed: int = 0, poison: bool = True, append: bool = False,
            free_fraction: float = 0.10, table_pad: int = 0, scale: Optional[float] = None,
@@ -282,4 +296,5 @@ WORKLOADS = {
     "mixed_bs32": lambda **kw: mixed_batch(block_size=32, **kw),
     "shared_prefix": shared_prefix,
     "llama70b_gqa": llama70b_gqa,
+    "llama70b_tp8": llama70b_tp8,
 }

@@ -12,13 +12,15 @@ import bench  # noqa: E402
 from paged_kv_cache_405_amd import binding as B  # noqa: E402
 from paged_kv_cache_405_amd import workloads as W  # noqa: E402
 
-BENCH_WORKLOADS = ["llama7b", "llama70b_gqa", "mixed_bs8", "mixed_bs16", "mixed_bs32", "shared_prefix"]
+BENCH_WORKLOADS = ["llama7b", "llama70b_gqa", "llama70b_tp8", "mixed_bs8", "mixed_bs16", "mixed_bs32",
+                   "shared_prefix"]
 
 
 @pytest.fixture(scope="module")
 def made():
     # the smallest instances of each shape keep this quick
-    small = {"llama7b": dict(num_seqs=2), "llama70b_gqa": dict(num_seqs=2), "shared_prefix": dict(num_seqs=2),
+    small = {"llama7b": dict(num_seqs=2), "llama70b_gqa": dict(num_seqs=2), "llama70b_tp8": dict(num_seqs=2),
+             "shared_prefix": dict(num_seqs=2),
              "mixed_bs8": dict(num_seqs=4), "mixed_bs16": dict(num_seqs=4), "mixed_bs32": dict(num_seqs=4)}
     out = {}
     for name in BENCH_WORKLOADS:
@@ -34,7 +36,7 @@ def test_default_run_settings(made, name):
     w = made[name]
     cfg = bench.run_config(args, w, B)
     assert cfg["pt"] == B.PA_PARTITION_AUTO and cfg["kern"] == B.PA_KERNEL_AUTO
-    assert cfg["layers"] == (80 if name == "llama70b_gqa" else 32)
+    assert cfg["layers"] == (80 if name.startswith("llama70b") else 32)
     assert cfg["shared"] == (name == "shared_prefix")
     # what the timed loop reads from the workload
     for attr in ("block_tables", "context_lens", "slot_mapping", "new_k", "new_v", "q", "scale",

@@ -20,7 +20,8 @@ from tests.pa_harness import assert_close, compare, gpu_step, log, oracle_step, 
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = ["tiny_f32", "llama7b", "mixed_bs8", "mixed_bs16", "mixed_bs32", "shared_prefix", "llama70b_gqa"]
+WORKLOADS = ["tiny_f32", "llama7b", "mixed_bs8", "mixed_bs16", "mixed_bs32", "shared_prefix", "llama70b_gqa",
+             "llama70b_tp8"]
 
 
 @pytest.fixture(scope="module")
@@ -205,3 +206,22 @@ def test_shared_blocks_flag_changes_no_bit(kernel, pt):
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert_close(compare(a, oracle_step(w), w.dtype), w.dtype, f"shared blocks kernel={kernel} pt={pt}")
+
+
+@pytest.mark.parametrize("kernel", [B.PA_KERNEL_VECTOR, B.PA_KERNEL_MFMA])
+def test_longest_first_windows(kernel):
+    """The grid kernels take each window of 64 sequences longest first: 150
+    sequences (two full windows and a ragged one of 22), many equal lengths
+    (ties go by index), a table long enough that the ordering is on; single
+    pass and split-K write every sequence's own rows."""
+    rng = np.random.default_rng(77)
+    ctxs = [int(c) for c in rng.choice([1, 16, 17, 300, 700, 1000], size=150)]
+    ctxs[149] = 1000        # the longest in the last, ragged window
+    ctxs[64] = 1            # the second window opens on one of many equal short lengths
+    w = W.custom(f"order_{kernel}", "bf16", ctxs, 16, 2, 128, 16, seed=78, append=True, table_pad=1)
+    log(f"[gpu] {w.name}")
+    g = upload(w)
+    for pt in (-1, 512):
+        out = gpu_step(w, g, partition_tokens=pt, kernel=kernel, append=(pt == -1))
+        torch.cuda.synchronize()
+        assert_close(compare(out, oracle_step(w), "bf16"), "bf16", f"{w.name} pt={pt}")
