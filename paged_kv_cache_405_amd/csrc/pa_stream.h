@@ -218,11 +218,12 @@ void decode_stream_kernel(const DecodeParams P)
 
 // Merge the pieces of every unit the stream kernel cut: one wave per (unit,
 // head of the unit), grid x = sequence, y = head group, z = head.  The piece
-// list is known from its two ends, so no load waits on another: first the
-// reference max over the pieces (lanes over pieces), then the weights (lane i
-// weighs piece i of a round of 64) and the rescaled sums over the round's
-// pieces in batches of FEW_PIECES, each batch's loads all in flight at once
-// (lanes over dims).  Pieces are added in order, so results are
+// list is known from its two ends, so no load waits on another: lane i loads
+// the (max, sum) of piece i and the wave the outputs of the first FEW_PIECES
+// pieces (lanes over dims), all at once; then the reference max, the weights
+// and the rescaled sums, with further batches of FEW_PIECES outputs as needed
+// (past 64 pieces, rounds of 64 weights, the max taken in a pass of its
+// own).  Pieces are added in order, so results are
 // bit-reproducible.  A unit of a small batch can be cut over many waves (32
 // sequences of one kv head over 1024 waves: about 33 pieces each); with one
 // load in flight per piece its merge took 32 us, batched it takes a few.
@@ -256,23 +257,25 @@ __global__ __launch_bounds__(64) void stream_reduce_kernel(const DecodeParams P,
         A[e] = 0.f;
     const int np = w1 - w0 + 1;
 
-    // the reference max: one piece per lane, 64 at a time
+    // the reference max: beyond 64 pieces a pass of its own (one piece per
+    // lane, 64 at a time); up to 64 from the weights' own loads below, taken
+    // once the first batch of outputs is in flight
+    const bool one_round = np <= 64;
     float M = NEG_BIG;
-    for (int w = w0 + lane; w <= w1; w += 64)
-        if (!empty(w))
-            M = fmaxf(M, P.piece_ml[slot(w)].x);
-    M = group_max<64>(M);
+    if (!one_round) {
+        for (int w = w0 + lane; w <= w1; w += 64)
+            if (!empty(w))
+                M = fmaxf(M, P.piece_ml[slot(w)].x);
+        M = group_max<64>(M);
+    }
 
     float L = 0.f;
     for (int r0 = 0; r0 < np; r0 += 64) {
         // lane i weighs piece r0 + i (an empty range left no piece: weight 0)
         const int wl = w0 + r0 + lane;
+        const bool has = r0 + lane < np && !empty(wl);
+        const float2 ml = has ? P.piece_ml[slot(wl)] : make_float2(NEG_BIG, 0.f);
         float c = 0.f;
-        if (r0 + lane < np && !empty(wl)) {
-            const float2 ml = P.piece_ml[slot(wl)];
-            c = fast_exp2(ml.x - M);
-            L = fmaf(ml.y, c, L);
-        }
         const int cnt = min(64, np - r0);
         for (int b0 = 0; b0 < cnt; b0 += FEW_PIECES) {
             // every load of the batch first; a piece past the end or of an
@@ -285,6 +288,12 @@ __global__ __launch_bounds__(64) void stream_reduce_kernel(const DecodeParams P,
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     a[i][e] = ok && lane + 64 * e < D ? P.piece_acc[slot(w) * D + lane + 64 * e] : 0.f;
+            }
+            if (b0 == 0) {
+                if (one_round)
+                    M = group_max<64>(ml.x);
+                c = has ? fast_exp2(ml.x - M) : 0.f;
+                L = fmaf(ml.y, c, L);
             }
 #pragma unroll
             for (int i = 0; i < FEW_PIECES; ++i) {
