@@ -26,6 +26,8 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+REPEATS = 5                 # back-to-back passes over all layers, for the median and the best
+WARM_CALLS = 20             # decode calls on one layer's pool, for the warm (cached) figure
 METRIC = "paged decode attention KV GB/s (% of HBM peak) and seq-layers/s, 1×MI355X"
 
 
@@ -370,6 +372,20 @@ def copy_calibration():
                                            "dispatches": 3}}), flush=True)
 
 
+def cpu_baseline_one_core(name, target_s):
+    """The same oracle sample on one host core: a child process with OMP_NUM_THREADS=1."""
+    import subprocess
+    code = ("import json, sys; sys.path.insert(0, %r); import bench; from paged_kv_cache_405_amd import workloads as W; "
+            "r = bench.cpu_baseline(W.WORKLOADS[%r](poison=False), %r); "
+            "print(json.dumps({k: r[k] for k in ('value', 'unit', 'cores', 'seq_layers_per_s', 'seconds')}))"
+            % (os.path.dirname(os.path.abspath(__file__)), name, float(target_s)))
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError(f"one-core oracle sample failed: {r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def cpu_baseline(w, target_s):
     """Time the CPU oracle (as it is) on a bounded sample of the same workload."""
     import oracle
@@ -569,6 +585,32 @@ def main():
     avg_call_ms = d0.elapsed_time(d1) / (args.steps * layers)
     log(f"[bench] decode calls back to back: {avg_call_ms * 1e3:.2f} us per call")
 
+    def back_to_back(fn, n):
+        """Average duration of n calls of fn() issued back to back between one event pair."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def all_layers(fn):
+        return lambda: [fn(*L) for L in Ls]
+
+    # the same back-to-back pass over every layer, repeated: median and best
+    reps = [back_to_back(all_layers(lambda kc, vc, q, nk, nv, out: decode(out, q, kc, vc)), 1) / layers
+            for _ in range(REPEATS)]
+    # the append kernel alone, every layer once per pass
+    append_us = back_to_back(all_layers(lambda kc, vc, q, nk, nv, out: B.pa_reshape_and_cache(
+        nk, nv, kc, vc, slots, layout=layout, stream=stream)), args.steps) / layers
+    # warm: layer 0's pool again and again (it can then sit in the caches: not a decode step);
+    # few calls, so that a kernel trace's average over the run stays that of the real step
+    kc, vc, q, _, _, out = Ls[0]
+    warm_us = back_to_back(lambda: decode(out, q, kc, vc), WARM_CALLS)
+    log(f"[bench] back-to-back passes: median {statistics.median(reps):.2f} us, best {min(reps):.2f} us per call; "
+        f"append alone {append_us:.2f} us; warm same pool {warm_us:.2f} us")
+
     # HBM bytes per call from the committed counter record, when it was taken
     # on these kernel sources (else null)
     from paged_kv_cache_405_amd import traffic as TR
@@ -625,11 +667,16 @@ def main():
             "bytes_per_call": roof_bytes,
         },
         "append_and_decode_us_per_layer": round(total_ms * 1e3 / calls, 3),
+        "append_us": round(append_us, 3),
+        "call_us_repeats": {"n": REPEATS, "median": round(statistics.median(reps), 3), "best": round(min(reps), 3),
+                            "what": "all layers' decode calls back to back, one event pair per pass"},
+        "warm_same_pool_call_us": round(warm_us, 3),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         cw = W.WORKLOADS[args.workload](poison=False)
         result["cpu_baseline"] = cpu_baseline(cw, args.cpu_seconds)
+        result["cpu_baseline"]["one_core"] = cpu_baseline_one_core(args.workload, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
