@@ -34,7 +34,8 @@
  *     after a call returns and has no global mutable state; calls are
  *     re-entrant and may run concurrently on different streams.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *     Calls only enqueue work; they never synchronise.
+ *     Calls only enqueue work; they never synchronise.  A call's kernels can
+ *     therefore be captured in a graph on `stream` and replayed.
  *   - Every argument check runs on the host before any HIP call.  A return
  *     other than PA_OK means nothing was enqueued.  PA_ERR_HIP reports a
  *     failed launch (for example: no GPU); device faults surface at the
