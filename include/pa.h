@@ -31,8 +31,9 @@
  * Common conventions
  *   - Device pointers are owned by the caller and must stay valid until the
  *     work enqueued on `stream` has finished.  The library keeps no pointer
- *     after a call returns and has no global mutable state; calls are
- *     re-entrant and may run concurrently on different streams.
+ *     after a call returns; its only global state is a mutex-guarded cache
+ *     of occupancy queries per (device, kernel shape), filled on first use.
+ *     Calls are re-entrant and may run concurrently on different streams.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work; they never synchronise.  A call's kernels can
  *     therefore be captured in a graph on `stream` and replayed.
