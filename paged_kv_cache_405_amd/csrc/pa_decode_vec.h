@@ -10,17 +10,19 @@
 // the max grows.  Partitions of one context (split-K) are merged the same way.
 //
 // Work decomposition (one workgroup per (partition, kv-head group, sequence)):
-//   - a wave reads a whole (block, kv head) tile of K and of V with 16-byte
-//     loads: lane -> (token row, 16-byte chunk of head_dim); LPT lanes cover
-//     one token's row, so a wave-wide load covers TPL = 64/LPT tokens;
+//   - a wave reads a step -- NLD wave-wide loads of K and of V, a slab of one
+//     (block, kv head) tile -- with 16-byte loads: lane -> (token row, 16-byte
+//     chunk of head_dim); LPT lanes cover one token's row, so a wave-wide load
+//     covers TPL = 64/LPT tokens;
 //   - q.k is a per-lane dot over the lane's chunk followed by a DPP sum over
 //     the LPT lanes of the row (no LDS);
 //   - each token row keeps its own (m, l, acc) over the tokens it sees; the
 //     rows are merged with cross-lane shuffles after the block loop, and the
 //     waves of the workgroup through LDS;
-//   - the waves of a workgroup take the partition's blocks round robin, and
-//     each wave issues the next block's loads before it computes the current
-//     one (register double buffering), so two blocks per wave are in flight.
+//   - the waves of a workgroup take the partition's steps round robin, and
+//     each wave issues the next step's loads before it computes the current
+//     one (register double buffering), so two steps per wave are in flight;
+//     no step past the last context token is read.
 //   - GT q heads that share one kv head (grouped-query attention) are handled
 //     by one workgroup, so each K/V element is read once per GT heads.
 //

@@ -37,13 +37,16 @@ hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t st);
 hipError_t launch_prefill_f16(const DecodeParams &p, int head_dim, int block_size, int max_query_len, hipStream_t st);
 hipError_t launch_prefill_bf16(const DecodeParams &p, int head_dim, int block_size, int max_query_len, hipStream_t st);
 // shared-prefix decode, first pass: the prefix's split-K partitions 0 .. first_partition - 1,
-// one per SHARED_PREFIX_CHUNK tokens of the prefix (the kernel's chunk)
-#ifndef PA_PREFIX_CHUNK
-#define PA_PREFIX_CHUNK 256
-#endif
-constexpr int SHARED_PREFIX_CHUNK = PA_PREFIX_CHUNK;
+// one per chunk of the prefix; a chunk is a multiple of 32 tokens in [SHARED_PREFIX_CHUNK_MIN,
+// SHARED_PREFIX_CHUNK_MAX], chosen per call
+constexpr int SHARED_PREFIX_CHUNK_MIN = 128;
+constexpr int SHARED_PREFIX_CHUNK_MAX = 512;
 constexpr int SHARED_PREFIX_SUFFIX_PARTITION = 512;   // tokens per split-K partition after the prefix
-hipError_t launch_prefix_f16(const DecodeParams &p, int head_dim, int block_size, int prefix_tokens, hipStream_t st);
-hipError_t launch_prefix_bf16(const DecodeParams &p, int head_dim, int block_size, int prefix_tokens, hipStream_t st);
+hipError_t launch_prefix_f16(const DecodeParams &p, int head_dim, int block_size, int prefix_tokens, int chunk,
+                             hipStream_t st);
+hipError_t launch_prefix_bf16(const DecodeParams &p, int head_dim, int block_size, int prefix_tokens, int chunk,
+                              hipStream_t st);
+// workgroups the prefix pass starts per chunk of the prefix
+int prefix_workgroups(int num_seqs, int group, int group_split, int num_kv_heads);
 
 }  // namespace pa

@@ -236,20 +236,26 @@ hipError_t launch_prefill_shape(const DecodeParams &p, int max_query_len, hipStr
 // 的基础"), those blocks' K/V need to be read once, not once per sequence:
 // the batch's query rows are the columns of one pass over them, like a
 // prefill's rows but with no causal order -- each sequence sees the prefix
-// tokens below its own context.  The prefix is cut into chunks of PX_CHUNK
-// tokens, one workgroup per (group of PF_WAVES column tiles, chunk, head
-// group); each (sequence, q head) leaves the chunk's (max, sum, unnormalised
-// output) as split-K partition `chunk`.  The decode kernels then take the
-// sequences' own blocks as the partitions after these, and the split-K reduce
-// merges them all.
-#ifndef PA_PREFIX_CHUNK
-#define PA_PREFIX_CHUNK 256
-#endif
-constexpr int PX_CHUNK = PA_PREFIX_CHUNK;   // prefix tokens per chunk (a multiple of two tiles; SHARED_PREFIX_CHUNK)
+// tokens below its own context.  The prefix is cut into chunks of `chunk`
+// tokens (a multiple of two tiles, chosen per call by the host), one
+// workgroup per (group of PF_WAVES column tiles, chunk, head group); each
+// (sequence, q head) leaves the chunk's (max, sum, unnormalised output) as
+// split-K partition `chunk`.  The decode kernels then take the sequences' own
+// blocks as the partitions after these, and the split-K reduce merges them
+// all.
+
+// workgroups the prefix pass starts per chunk: column groups x head groups
+inline int prefix_workgroups_per_chunk(int num_seqs, int group, int group_split, int num_kv_heads)
+{
+    const int rows = GQA_TILE / (group / group_split);
+    const int col_tiles = (num_seqs + rows - 1) / rows;
+    const int col_groups = (col_tiles + PF_WAVES - 1) / PF_WAVES;
+    return col_groups * num_kv_heads * group_split;
+}
 
 template <typename T, int D, int BS>
 __global__ __launch_bounds__(PF_WAVES * 64) void prefix_kernel(const DecodeParams P, int col_groups, int n_chunks,
-                                                               int prefix_tokens, int total_wg)
+                                                               int prefix_tokens, int chunk, int total_wg)
 {
     static_assert(D % 128 == 0, "the matrix-core worker needs head_dim 128 or 256");
     using PT = PrefillTiles<T, D, BS, false>;
@@ -271,8 +277,8 @@ __global__ __launch_bounds__(PF_WAVES * 64) void prefix_kernel(const DecodeParam
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i0 = i0g + wave * rows;
     const bool active = i0 < P.num_seqs;
-    const int c0 = c * PX_CHUNK;
-    const int c1 = min(prefix_tokens, c0 + PX_CHUNK);
+    const int c0 = c * chunk;
+    const int c1 = min(prefix_tokens, c0 + chunk);
     W w;
     w.init_lane(lane);
     w.bind_prefix(P, hg, active ? i0 : i0g, c0, c1);
@@ -285,12 +291,14 @@ __global__ __launch_bounds__(PF_WAVES * 64) void prefix_kernel(const DecodeParam
 }
 
 template <typename T, int D, int BS>
-hipError_t launch_prefix_shape(const DecodeParams &p, int prefix_tokens, hipStream_t st)
+hipError_t launch_prefix_shape(const DecodeParams &p, int prefix_tokens, int chunk, hipStream_t st)
 {
+    if (chunk <= 0 || chunk % (2 * GQA_TILE) != 0)
+        return hipErrorInvalidValue;
     const int rows = GQA_TILE / (p.group / p.group_split);
     const int col_tiles = (p.num_seqs + rows - 1) / rows;
     const int col_groups = (col_tiles + PF_WAVES - 1) / PF_WAVES;
-    const int n_chunks = (prefix_tokens + PX_CHUNK - 1) / PX_CHUNK;
+    const int n_chunks = (prefix_tokens + chunk - 1) / chunk;
     if (n_chunks != p.first_partition)
         return hipErrorInvalidValue;
     const long long total = (long long)col_groups * n_chunks * p.num_kv_heads * p.group_split;
@@ -298,20 +306,21 @@ hipError_t launch_prefix_shape(const DecodeParams &p, int prefix_tokens, hipStre
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)((total + 7) / 8 * 8));
     hipLaunchKernelGGL((prefix_kernel<T, D, BS>), grid, dim3(PF_WAVES * 64), 0, st, p, col_groups, n_chunks,
-                       prefix_tokens, (int)total);
+                       prefix_tokens, chunk, (int)total);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_prefix_dtype(const DecodeParams &p, int head_dim, int bs, int prefix_tokens, hipStream_t st)
+hipError_t launch_prefix_dtype(const DecodeParams &p, int head_dim, int bs, int prefix_tokens, int chunk,
+                               hipStream_t st)
 {
     switch (head_dim * 64 + bs) {
-    case 128 * 64 + 8: return launch_prefix_shape<T, 128, 8>(p, prefix_tokens, st);
-    case 128 * 64 + 16: return launch_prefix_shape<T, 128, 16>(p, prefix_tokens, st);
-    case 128 * 64 + 32: return launch_prefix_shape<T, 128, 32>(p, prefix_tokens, st);
-    case 256 * 64 + 8: return launch_prefix_shape<T, 256, 8>(p, prefix_tokens, st);
-    case 256 * 64 + 16: return launch_prefix_shape<T, 256, 16>(p, prefix_tokens, st);
-    case 256 * 64 + 32: return launch_prefix_shape<T, 256, 32>(p, prefix_tokens, st);
+    case 128 * 64 + 8: return launch_prefix_shape<T, 128, 8>(p, prefix_tokens, chunk, st);
+    case 128 * 64 + 16: return launch_prefix_shape<T, 128, 16>(p, prefix_tokens, chunk, st);
+    case 128 * 64 + 32: return launch_prefix_shape<T, 128, 32>(p, prefix_tokens, chunk, st);
+    case 256 * 64 + 8: return launch_prefix_shape<T, 256, 8>(p, prefix_tokens, chunk, st);
+    case 256 * 64 + 16: return launch_prefix_shape<T, 256, 16>(p, prefix_tokens, chunk, st);
+    case 256 * 64 + 32: return launch_prefix_shape<T, 256, 32>(p, prefix_tokens, chunk, st);
     default: return hipErrorInvalidValue;
     }
 }

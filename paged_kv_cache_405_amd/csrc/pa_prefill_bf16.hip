@@ -9,9 +9,10 @@ hipError_t launch_prefill_bf16(const DecodeParams &p, int head_dim, int block_si
     return launch_prefill_dtype<bf16_t>(p, head_dim, block_size, max_query_len, st);
 }
 
-hipError_t launch_prefix_bf16(const DecodeParams &p, int head_dim, int block_size, int prefix_tokens, hipStream_t st)
+hipError_t launch_prefix_bf16(const DecodeParams &p, int head_dim, int block_size, int prefix_tokens, int chunk,
+                              hipStream_t st)
 {
-    return launch_prefix_dtype<bf16_t>(p, head_dim, block_size, prefix_tokens, st);
+    return launch_prefix_dtype<bf16_t>(p, head_dim, block_size, prefix_tokens, chunk, st);
 }
 
 }  // namespace pa
