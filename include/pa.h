@@ -298,6 +298,39 @@ pa_status pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_he
                                     int partition_tokens, size_t *bytes_out);
 
 /*
+ * pa_decode_append -- one decode step in one call: append each sequence's new
+ * K/V row, then attend ("vLLM 与 PagedAttention" section 二: a step writes its
+ * token into the last block, which is taken only when the previous one is
+ * full, and attention then reads the whole block chain).  Same result, bit for
+ * bit in the pool and within the decode's bounds in out, as
+ * pa_reshape_and_cache(k_new, v_new, ..., slot_mapping, num_seqs, ...)
+ * followed by pa_decode_ex(...) with the same arguments.
+ *
+ *   k_new, v_new   [num_seqs, num_kv_heads, head_dim] dtype, contiguous: the
+ *                  new row of sequence s is token s
+ *   k_cache,
+ *   v_cache        written at the mapped slots, then read
+ *   slot_mapping   [num_seqs] int64: sequence s's new row goes to slot
+ *                  slot_mapping[s] (skipped when negative or past the pool);
+ *                  it must lie in a block that no other sequence of the call
+ *                  reads (the sequence's own last block, as copy-on-write
+ *                  leaves it)
+ *   other arguments as for pa_decode_ex; context_lens count the new token
+ *
+ * On the single-pass vector path (what PA_PARTITION_AUTO picks for
+ * multi-head attention with many sequences) the append runs inside the decode
+ * kernel: one launch per step.  On every other path, and with
+ * PA_DECODE_SHARED_BLOCKS, the append kernel is enqueued first.  Every
+ * argument is checked before anything is enqueued.
+ */
+pa_status pa_decode_append(void *out, const void *q, const void *k_new, const void *v_new, void *k_cache,
+                           void *v_cache, const int64_t *slot_mapping, const int32_t *block_tables,
+                           const int32_t *context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                           pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
+                           unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pa_reshape_and_cache -- append new K/V rows into the pool.
  *
  *   k, v           [num_tokens, num_kv_heads, head_dim] dtype, contiguous

@@ -65,6 +65,8 @@ def lib():
             L.pa_decode.argtypes = [vp] * 6 + [i32] * 6 + [f32, i32, vp, sz, vp]
             L.pa_decode_ex.restype = i32
             L.pa_decode_ex.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, i32, i32, ctypes.c_uint32, vp, sz, vp]
+            L.pa_decode_append.restype = i32
+            L.pa_decode_append.argtypes = [vp] * 9 + [i32] * 7 + [f32, i32, i32, i32, i32, ctypes.c_uint32, vp, sz, vp]
             L.pa_decode_shared_prefix.restype = i32
             L.pa_decode_shared_prefix.argtypes = [vp] * 6 + [i32] * 8 + [f32, i32, i32, vp, sz, vp]
             L.pa_decode_shared_prefix_workspace_bytes.restype = i32
@@ -226,6 +228,37 @@ def pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, *,
         None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode_ex")
+    return out
+
+
+def pa_decode_append(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens, scale, *,
+                     num_blocks=None, layout=PA_LAYOUT_BHTD, partition_tokens=0, kernel=PA_KERNEL_AUTO,
+                     shared_blocks=False, workspace=None, stream=None):
+    """One decode step: sequence s's new K/V rows k_new/v_new[s] go to slot slot_mapping[s], then
+    out[S, Hq, D] <- paged decode attention of q over the caches (context_lens count the new token)."""
+    torch = _torch()
+    code = _dtype_code(q)
+    S, Hq, D = q.shape
+    NB, bs, Hkv, D2 = cache_dims(k_cache, layout)
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, out and the caches")
+    if tuple(k_new.shape) != (S, Hkv, D) or tuple(v_new.shape) != (S, Hkv, D) or tuple(slot_mapping.shape) != (S,):
+        raise ValueError("k_new, v_new must be [S, Hkv, D] and slot_mapping [S]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    MB = block_tables.shape[1]
+    nbytes = pa_decode_workspace_bytes(S, Hq, Hkv, D, bs, MB, code, partition_tokens)
+    ws, ws_bytes = _workspace(q, nbytes, workspace)
+    st = lib().pa_decode_append(
+        _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype),
+        _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        _dev(slot_mapping, "slot_mapping", torch.int64), _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32),
+        S, Hq, Hkv, D, bs, MB, NB if num_blocks is None else int(num_blocks), float(scale), code, int(layout),
+        int(partition_tokens), int(kernel), PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
+        None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_append")
     return out
 
 

@@ -208,57 +208,31 @@ int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-pa_status pa_decode_path(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                         int max_blocks_per_seq, pa_dtype dtype, int partition_tokens, pa_kernel kernel,
-                         int *partition_out, pa_kernel *kernel_out)
-{
-    if (!partition_out || !kernel_out)
-        return PA_ERR_INVALID_ARG;
-    Plan pl;
-    const pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                   max_blocks_per_seq, dtype, partition_tokens, kernel, &pl);
-    if (st != PA_OK)
-        return st;
-    *partition_out = pl.stream ? PA_PARTITION_BALANCED
-                   : pl.max_partitions > 1 ? pl.partition_blocks * block_size : PA_PARTITION_SINGLE;
-    *kernel_out = pl.mfma ? PA_KERNEL_MFMA : PA_KERNEL_VECTOR;
-    return PA_OK;
-}
+// The new K/V rows of a decode step: one token per sequence, sequence s's
+// rows k_new/v_new[s] going to slot slots[s] (pa_decode_append).
+struct AppendRows {
+    const void *k_new;
+    const void *v_new;
+    const int64_t *slots;
+};
 
-pa_status pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                    int block_size, int max_blocks_per_seq, pa_dtype dtype,
-                                    int partition_tokens, size_t *bytes_out)
-{
-    if (!bytes_out)
-        return PA_ERR_INVALID_ARG;
-    // enough for whichever kernel the call picks
-    *bytes_out = 0;
-    Plan pl;
-    pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                             max_blocks_per_seq, dtype, partition_tokens, PA_KERNEL_VECTOR, &pl);
-    if (st != PA_OK)
-        return st;
-    size_t bytes = pl.ws_bytes;
-    if (mfma_shape(dtype, head_dim, num_q_heads / num_kv_heads)) {
-        Plan pm;
-        st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
-                       partition_tokens, PA_KERNEL_MFMA, &pm);
-        if (st != PA_OK)
-            return st;
-        bytes = pm.ws_bytes > bytes ? pm.ws_bytes : bytes;
-    }
-    *bytes_out = bytes;
-    return PA_OK;
-}
+pa_status launch_append_rows(const void *k, const void *v, void *k_cache, void *v_cache, const int64_t *slots,
+                             int num_tokens, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             pa_dtype dtype, pa_layout layout, hipStream_t stream);
 
-pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_cache,
-                       const int32_t *block_tables, const int32_t *context_lens,
-                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                       int block_size, int max_blocks_per_seq, int num_blocks, float scale,
-                       pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
-                       unsigned flags, void *workspace, size_t workspace_bytes, void *stream)
+// pa_decode_ex, and pa_decode_append when app is given: every argument is
+// checked before anything is enqueued; the append is folded into the decode
+// kernel on the single-pass vector path (a step whose new rows no other
+// sequence reads: not with PA_DECODE_SHARED_BLOCKS), else enqueued as the
+// append kernel ahead of the decode
+pa_status decode_call(void *out, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                      pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
+                      unsigned flags, void *workspace, size_t workspace_bytes, void *stream, const AppendRows *app)
 {
     if (flags & ~(unsigned)PA_DECODE_SHARED_BLOCKS)
         return PA_ERR_INVALID_ARG;
@@ -326,6 +300,18 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    if (app) {
+        if (!pl.stream && !pl.mfma && pl.max_partitions == 1 && !(flags & PA_DECODE_SHARED_BLOCKS)) {
+            p.new_k = app->k_new;
+            p.new_v = app->v_new;
+            p.append_slots = app->slots;
+            p.num_slots = (int64_t)num_blocks * block_size;
+        } else if (launch_append_rows(app->k_new, app->v_new, const_cast<void *>(k_cache),
+                                      const_cast<void *>(v_cache), app->slots, num_seqs, num_kv_heads, head_dim,
+                                      block_size, num_blocks, dtype, layout, s) != PA_OK) {
+            return PA_ERR_HIP;
+        }
+    }
     if (pl.stream) {
         if (pl.mfma)
             e = dtype == PA_F16 ? pa::stream_mfma_f16(&p, head_dim, block_size, s, nullptr)
@@ -358,6 +344,82 @@ pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void
             return PA_ERR_HIP;
     }
     return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_path(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                         int max_blocks_per_seq, pa_dtype dtype, int partition_tokens, pa_kernel kernel,
+                         int *partition_out, pa_kernel *kernel_out)
+{
+    if (!partition_out || !kernel_out)
+        return PA_ERR_INVALID_ARG;
+    Plan pl;
+    const pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, dtype, partition_tokens, kernel, &pl);
+    if (st != PA_OK)
+        return st;
+    *partition_out = pl.stream ? PA_PARTITION_BALANCED
+                   : pl.max_partitions > 1 ? pl.partition_blocks * block_size : PA_PARTITION_SINGLE;
+    *kernel_out = pl.mfma ? PA_KERNEL_MFMA : PA_KERNEL_VECTOR;
+    return PA_OK;
+}
+
+pa_status pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int max_blocks_per_seq, pa_dtype dtype,
+                                    int partition_tokens, size_t *bytes_out)
+{
+    if (!bytes_out)
+        return PA_ERR_INVALID_ARG;
+    // enough for whichever kernel the call picks
+    *bytes_out = 0;
+    Plan pl;
+    pa_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, dtype, partition_tokens, PA_KERNEL_VECTOR, &pl);
+    if (st != PA_OK)
+        return st;
+    size_t bytes = pl.ws_bytes;
+    if (mfma_shape(dtype, head_dim, num_q_heads / num_kv_heads)) {
+        Plan pm;
+        st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
+                       partition_tokens, PA_KERNEL_MFMA, &pm);
+        if (st != PA_OK)
+            return st;
+        bytes = pm.ws_bytes > bytes ? pm.ws_bytes : bytes;
+    }
+    *bytes_out = bytes;
+    return PA_OK;
+}
+
+pa_status pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                       pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
+                       unsigned flags, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return decode_call(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, max_blocks_per_seq, num_blocks, scale, dtype, layout, partition_tokens,
+                       kernel, flags, workspace, workspace_bytes, stream, nullptr);
+}
+
+pa_status pa_decode_append(void *out, const void *q, const void *k_new, const void *v_new, void *k_cache,
+                           void *v_cache, const int64_t *slot_mapping, const int32_t *block_tables,
+                           const int32_t *context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                           pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
+                           unsigned flags, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8))
+        return PA_ERR_INVALID_ARG;
+    const AppendRows app{k_new, v_new, slot_mapping};
+    return decode_call(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, max_blocks_per_seq, num_blocks, scale, dtype, layout, partition_tokens,
+                       kernel, flags, workspace, workspace_bytes, stream, &app);
 }
 
 pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -561,21 +623,8 @@ pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void
         !aligned(slot_mapping, 8))
         return PA_ERR_INVALID_ARG;
 
-    pa::AppendParams a;
-    std::memset(&a, 0, sizeof(a));
-    a.k = k;
-    a.v = v;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.slots = slot_mapping;
-    layout_strides(layout, num_kv_heads, block_size, head_dim, &a.block_stride, &a.head_stride, &a.token_stride);
-    a.num_tokens = num_tokens;
-    a.num_kv_heads = num_kv_heads;
-    a.block_size = block_size;
-    a.num_slots = (int64_t)num_blocks * block_size;
-    a.elem_bytes = elem_bytes(dtype);
-    a.chunks_per_head = head_dim * a.elem_bytes / 16;
-    return pa::launch_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+    return launch_append_rows(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                              block_size, num_blocks, dtype, layout, static_cast<hipStream_t>(stream));
 }
 
 pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -720,6 +769,33 @@ const char *pa_status_string(pa_status status)
     }
 }
 
-int pa_abi_version(void) { return 200; }
+int pa_abi_version(void) { return 201; }
 
 }  // extern "C"
+
+namespace {
+
+// the append kernel over num_tokens new rows (arguments already checked)
+pa_status launch_append_rows(const void *k, const void *v, void *k_cache, void *v_cache, const int64_t *slots,
+                             int num_tokens, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             pa_dtype dtype, pa_layout layout, hipStream_t stream)
+{
+    pa::AppendParams a;
+    std::memset(&a, 0, sizeof(a));
+    a.k = k;
+    a.v = v;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.slots = slots;
+    layout_strides(layout, num_kv_heads, block_size, head_dim, &a.block_stride, &a.head_stride, &a.token_stride);
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.num_slots = (int64_t)num_blocks * block_size;
+    a.elem_bytes = elem_bytes(dtype);
+    a.chunks_per_head = head_dim * a.elem_bytes / 16;
+    return pa::launch_append(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+

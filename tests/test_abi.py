@@ -42,7 +42,7 @@ def test_status_strings_and_version(L):
         s = B.pa_status_string(code)
         assert isinstance(s, str) and s
     assert B.pa_status_string(99) == "unknown status"
-    assert B.pa_abi_version() == 200
+    assert B.pa_abi_version() == 201
 
 
 def _ws(S=4, Hq=8, Hkv=2, D=128, bs=16, MB=64, dt=B.PA_F16, pt=0):
@@ -289,3 +289,25 @@ def test_shared_prefix_workspace_query():
     assert L.pa_decode_shared_prefix_workspace_bytes(4, 8, 2, 128, 16, 10, B.PA_F16, 11, ctypes.byref(sz)) == \
         B.PA_ERR_INVALID_ARG
     assert L.pa_decode_shared_prefix_workspace_bytes(4, 8, 2, 128, 16, 10, B.PA_F16, 4, None) == B.PA_ERR_INVALID_ARG
+
+
+def _decode_append(**kw):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, sm=FAKE, bt=FAKE, cl=FAKE, S=2, Hq=4, Hkv=2, D=64,
+             bs=16, MB=8, NB=32, scale=0.125, dt=B.PA_F16, layout=B.PA_LAYOUT_BHTD, pt=512, kern=B.PA_KERNEL_AUTO,
+             flags=0, ws=None, wsb=0)
+    a.update(kw)
+    return B.lib().pa_decode_append(a["out"], a["q"], a["kn"], a["vn"], a["k"], a["v"], a["sm"], a["bt"], a["cl"],
+                                    a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["scale"],
+                                    a["dt"], a["layout"], a["pt"], a["kern"], a["flags"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=0, out=None, q=None, kn=None, vn=None, k=None, v=None, sm=None, bt=None, cl=None), B.PA_OK),
+    (dict(kn=None), B.PA_ERR_INVALID_ARG), (dict(vn=None), B.PA_ERR_INVALID_ARG), (dict(sm=None), B.PA_ERR_INVALID_ARG),
+    (dict(kn=FAKE + 8), B.PA_ERR_INVALID_ARG), (dict(sm=FAKE + 4), B.PA_ERR_INVALID_ARG),
+    (dict(q=None), B.PA_ERR_INVALID_ARG), (dict(D=48), B.PA_ERR_UNSUPPORTED), (dict(flags=8), B.PA_ERR_INVALID_ARG),
+    (dict(MB=64), B.PA_ERR_WORKSPACE),     # 2 split-K partitions need a workspace: refused before the append
+])
+def test_decode_append_checks_arguments_first(kw, status):
+    # every check runs before anything is enqueued (here: before any HIP call)
+    assert _decode_append(**kw) == status

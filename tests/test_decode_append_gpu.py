@@ -1,0 +1,70 @@
+"""GPU parity of pa_decode_append (one decode step in one call: the new K/V
+rows appended, then attention) against the oracle's append-then-decode, on
+the path where the append runs inside the decode kernel and on the paths
+where it is enqueued ahead of it; the pool afterwards is bit-identical to
+what the append kernel alone writes.  The appended tokens' slots hold NaN
+before the call, so a decode that read a slot before its row landed would
+show."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_405_amd import binding as B
+from paged_kv_cache_405_amd import workloads as W
+from tests.pa_harness import assert_close, compare, log, oracle_step, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32)
+
+
+CASES = [
+    # workload, partition, kernel, shared-blocks flag
+    ("tiny_f32", B.PA_PARTITION_SINGLE, B.PA_KERNEL_AUTO, False),      # fused
+    ("llama7b", B.PA_PARTITION_AUTO, B.PA_KERNEL_AUTO, False),         # fused (the library's choice)
+    ("mixed_bs8", B.PA_PARTITION_AUTO, B.PA_KERNEL_AUTO, False),       # fused
+    ("mixed_bs32", B.PA_PARTITION_SINGLE, B.PA_KERNEL_AUTO, False),    # fused
+    ("llama7b", B.PA_PARTITION_SINGLE, B.PA_KERNEL_AUTO, True),        # shared-blocks flag: append kernel first
+    ("llama7b", 512, B.PA_KERNEL_AUTO, False),                         # split-K: append kernel first
+    ("llama7b", B.PA_PARTITION_BALANCED, B.PA_KERNEL_AUTO, False),     # balanced: append kernel first
+    ("llama70b_gqa", B.PA_PARTITION_AUTO, B.PA_KERNEL_AUTO, False),    # matrix cores: append kernel first
+    ("llama70b_gqa", B.PA_PARTITION_SINGLE, B.PA_KERNEL_VECTOR, False),  # grouped heads on the vector path: fused
+]
+
+
+@pytest.mark.parametrize("name,pt,kernel,shared", CASES)
+def test_decode_append_matches_append_then_decode(name, pt, kernel, shared):
+    w = W.WORKLOADS[name]()
+    log(f"[gpu] decode_append {name} pt={pt} kernel={kernel} shared={shared}")
+    g = upload(w)
+    ref_k, ref_v = g.k_cache.clone(), g.v_cache.clone()
+    B.pa_reshape_and_cache(g.new_k, g.new_v, ref_k, ref_v, g.slots, layout=g.layout)
+    out = torch.full_like(g.q, float("nan"))
+    B.pa_decode_append(out, g.q, g.new_k, g.new_v, g.k_cache, g.v_cache, g.slots, g.tables, g.ctx, w.scale,
+                       layout=g.layout, partition_tokens=pt, kernel=kernel, shared_blocks=shared)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(g.k_cache), _bits(ref_k)) and torch.equal(_bits(g.v_cache), _bits(ref_v)), \
+        "the pool differs from the append kernel's"
+    assert_close(compare(out, oracle_step(w), w.dtype), w.dtype, f"{name} pt={pt}")
+
+
+def test_decode_append_skips_invalid_slots():
+    """A negative slot appends nothing (that sequence then attends its cached tokens only)."""
+    w = W.custom("append_skip", "f16", [40, 17, 300], 4, 4, 128, 16, seed=12, append=True, poison=False)
+    g = upload(w)
+    slots = g.slots.clone()
+    slots[1] = -1
+    before_k = g.k_cache.clone()
+    out = torch.empty_like(g.q)
+    B.pa_decode_append(out, g.q, g.new_k, g.new_v, g.k_cache, g.v_cache, slots, g.tables, g.ctx, w.scale,
+                       layout=g.layout, partition_tokens=B.PA_PARTITION_SINGLE)
+    torch.cuda.synchronize()
+    ref_k = before_k.clone()
+    ref_v = g.v_cache.clone()   # compare K only for the skipped row's block
+    B.pa_reshape_and_cache(g.new_k, g.new_v, ref_k, ref_v, slots, layout=g.layout)
+    assert torch.equal(_bits(g.k_cache), _bits(ref_k))
+    w2 = W.custom("append_skip", "f16", [40, 17, 300], 4, 4, 128, 16, seed=12, append=True, poison=False)
+    w2.slot_mapping = slots.cpu().numpy()
+    assert_close(compare(out, oracle_step(w2), "f16"), "f16", "negative slot")
