@@ -311,17 +311,15 @@ pa_status pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_he
  *   k_cache,
  *   v_cache        written at the mapped slots, then read
  *   slot_mapping   [num_seqs] int64: sequence s's new row goes to slot
- *                  slot_mapping[s] (skipped when negative or past the pool);
- *                  it must lie in a block that no other sequence of the call
- *                  reads (the sequence's own last block, as copy-on-write
- *                  leaves it)
+ *                  slot_mapping[s] (skipped when negative or past the pool)
  *   other arguments as for pa_decode_ex; context_lens count the new token
  *
- * On the single-pass vector path (what PA_PARTITION_AUTO picks for
- * multi-head attention with many sequences) the append runs inside the decode
- * kernel: one launch per step.  On every other path, and with
- * PA_DECODE_SHARED_BLOCKS, the append kernel is enqueued first.  Every
- * argument is checked before anything is enqueued.
+ * The append kernel is enqueued ahead of the decode, with every argument
+ * checked before either: a caller that cannot check the decode's arguments
+ * itself gets both steps or neither.  (Folding the append into the decode
+ * kernel -- the new row taken from registers where the step reads it --
+ * measured no faster on MI355X: 189.9 against 190.5 us per 7B-shaped step,
+ * 386.3 against 377.1 us on the mixed batch.)
  */
 pa_status pa_decode_append(void *out, const void *q, const void *k_new, const void *v_new, void *k_cache,
                            void *v_cache, const int64_t *slot_mapping, const int32_t *block_tables,

@@ -223,10 +223,8 @@ pa_status launch_append_rows(const void *k, const void *v, void *k_cache, void *
                              pa_dtype dtype, pa_layout layout, hipStream_t stream);
 
 // pa_decode_ex, and pa_decode_append when app is given: every argument is
-// checked before anything is enqueued; the append is folded into the decode
-// kernel on the single-pass vector path (a step whose new rows no other
-// sequence reads: not with PA_DECODE_SHARED_BLOCKS), else enqueued as the
-// append kernel ahead of the decode
+// checked before anything is enqueued, then the append kernel goes ahead of
+// the decode
 pa_status decode_call(void *out, const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, const int32_t *context_lens,
                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -300,18 +298,10 @@ pa_status decode_call(void *out, const void *q, const void *k_cache, const void 
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (app) {
-        if (!pl.stream && !pl.mfma && pl.max_partitions == 1 && !(flags & PA_DECODE_SHARED_BLOCKS)) {
-            p.new_k = app->k_new;
-            p.new_v = app->v_new;
-            p.append_slots = app->slots;
-            p.num_slots = (int64_t)num_blocks * block_size;
-        } else if (launch_append_rows(app->k_new, app->v_new, const_cast<void *>(k_cache),
-                                      const_cast<void *>(v_cache), app->slots, num_seqs, num_kv_heads, head_dim,
-                                      block_size, num_blocks, dtype, layout, s) != PA_OK) {
-            return PA_ERR_HIP;
-        }
-    }
+    if (app && launch_append_rows(app->k_new, app->v_new, const_cast<void *>(k_cache), const_cast<void *>(v_cache),
+                                  app->slots, num_seqs, num_kv_heads, head_dim, block_size, num_blocks, dtype,
+                                  layout, s) != PA_OK)
+        return PA_ERR_HIP;
     if (pl.stream) {
         if (pl.mfma)
             e = dtype == PA_F16 ? pa::stream_mfma_f16(&p, head_dim, block_size, s, nullptr)

@@ -292,37 +292,6 @@ struct VecWorker {
     }
 };
 
-// The step's append folded into the decode: the workgroup of sequence s and
-// kv head g copies s's new K and V rows of head g into their slot (bit for
-// bit, as the append kernel does; a slot outside the pool is skipped), and
-// every wave of the workgroup waits until the rows are visible before it
-// reads the sequence's blocks.  Only this workgroup reads that slot: the
-// slot lies in the sequence's own last block (the caller guarantees no other
-// sequence of the call reads that block), and workgroups that share a kv
-// head write the same bytes.
-template <typename T, int D, int BS>
-__device__ __forceinline__ void append_own_row(const DecodeParams &P, int s, int kvh)
-{
-    constexpr int ES = 16 / Vec<T>::N;
-    constexpr int CHUNKS = D * ES / 16;            // 16-byte pieces of one row
-    const int64_t slot = P.append_slots[s];
-    if (slot >= 0 && slot < P.num_slots) {
-        const int64_t b = slot / BS;
-        const int64_t off = slot - b * BS;
-        const int64_t row = ((int64_t)s * P.num_kv_heads + kvh) * (D * ES);
-        const int64_t dst = (b * P.block_stride + kvh * P.head_stride + off * P.token_stride) * ES;
-        for (int c = threadIdx.x; c < 2 * CHUNKS; c += blockDim.x) {
-            const bool is_v = c >= CHUNKS;
-            const int ch = is_v ? c - CHUNKS : c;
-            const char *src = static_cast<const char *>(is_v ? P.new_v : P.new_k) + row + ch * 16;
-            char *d = static_cast<char *>(const_cast<void *>(is_v ? P.v : P.k)) + dst + ch * 16;
-            st16(d, ld16(src));
-        }
-    }
-    __threadfence();
-    __syncthreads();
-}
-
 template <typename T, int D, int BS, int GT, int NW, bool STREAM_KV>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_VEC_WAVES_PER_EU)))
 void decode_vec_kernel(const DecodeParams P)
@@ -341,9 +310,6 @@ void decode_vec_kernel(const DecodeParams P)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-    if (P.new_k)
-        append_own_row<T, D, BS>(P, s, hg / P.group_split);
 
     W w;
     w.init_lane(lane);

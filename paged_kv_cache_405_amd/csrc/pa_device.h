@@ -325,12 +325,6 @@ struct DecodeParams {
     int n_waves;              // logical waves of the stream kernel (a multiple of 8)
     int kv_cached;            // 1: blocks may be shared across sequences -- plain (cached) K/V loads
     int order_rows;           // grid kernels: 1 = take sequences longest first (seq_of_row), 0 = in order
-    // decode with the step's append folded in (vector grid kernel): sequence s's
-    // new K/V rows new_k/new_v[s] go to slot append_slots[s] before it is read
-    const void *new_k;        // [num_seqs, num_kv_heads, D] (nullptr: no append)
-    const void *new_v;
-    const int64_t *append_slots;
-    int64_t num_slots;        // num_blocks * block_size
     const int32_t *query_start;   // multi-token calls: [num_seqs + 1] first q row of each sequence
     int total_q;                  // multi-token calls: rows of q and out
     uint64_t *stream_total;   // [1] steps of the whole stream (T), written by the stream kernel

@@ -1,10 +1,8 @@
 """GPU parity of pa_decode_append (one decode step in one call: the new K/V
 rows appended, then attention) against the oracle's append-then-decode, on
-the path where the append runs inside the decode kernel and on the paths
-where it is enqueued ahead of it; the pool afterwards is bit-identical to
-what the append kernel alone writes.  The appended tokens' slots hold NaN
-before the call, so a decode that read a slot before its row landed would
-show."""
+every decode path; the pool afterwards is bit-identical to what the append
+kernel alone writes.  The appended tokens' slots hold NaN before the call,
+so a decode that read a slot before its row landed would show."""
 import numpy as np
 import pytest
 import torch
@@ -22,15 +20,15 @@ def _bits(t):
 
 CASES = [
     # workload, partition, kernel, shared-blocks flag
-    ("tiny_f32", B.PA_PARTITION_SINGLE, B.PA_KERNEL_AUTO, False),      # fused
-    ("llama7b", B.PA_PARTITION_AUTO, B.PA_KERNEL_AUTO, False),         # fused (the library's choice)
-    ("mixed_bs8", B.PA_PARTITION_AUTO, B.PA_KERNEL_AUTO, False),       # fused
-    ("mixed_bs32", B.PA_PARTITION_SINGLE, B.PA_KERNEL_AUTO, False),    # fused
-    ("llama7b", B.PA_PARTITION_SINGLE, B.PA_KERNEL_AUTO, True),        # shared-blocks flag: append kernel first
-    ("llama7b", 512, B.PA_KERNEL_AUTO, False),                         # split-K: append kernel first
-    ("llama7b", B.PA_PARTITION_BALANCED, B.PA_KERNEL_AUTO, False),     # balanced: append kernel first
-    ("llama70b_gqa", B.PA_PARTITION_AUTO, B.PA_KERNEL_AUTO, False),    # matrix cores: append kernel first
-    ("llama70b_gqa", B.PA_PARTITION_SINGLE, B.PA_KERNEL_VECTOR, False),  # grouped heads on the vector path: fused
+    ("tiny_f32", B.PA_PARTITION_SINGLE, B.PA_KERNEL_AUTO, False),
+    ("llama7b", B.PA_PARTITION_AUTO, B.PA_KERNEL_AUTO, False),         # the library's choice
+    ("mixed_bs8", B.PA_PARTITION_AUTO, B.PA_KERNEL_AUTO, False),
+    ("mixed_bs32", B.PA_PARTITION_SINGLE, B.PA_KERNEL_AUTO, False),
+    ("llama7b", B.PA_PARTITION_SINGLE, B.PA_KERNEL_AUTO, True),        # shared-blocks flag
+    ("llama7b", 512, B.PA_KERNEL_AUTO, False),                         # split-K
+    ("llama7b", B.PA_PARTITION_BALANCED, B.PA_KERNEL_AUTO, False),     # balanced schedule
+    ("llama70b_gqa", B.PA_PARTITION_AUTO, B.PA_KERNEL_AUTO, False),    # matrix cores
+    ("llama70b_gqa", B.PA_PARTITION_SINGLE, B.PA_KERNEL_VECTOR, False),  # grouped heads on the vector path
 ]
 
 
@@ -68,3 +66,28 @@ def test_decode_append_skips_invalid_slots():
     w2 = W.custom("append_skip", "f16", [40, 17, 300], 4, 4, 128, 16, seed=12, append=True, poison=False)
     w2.slot_mapping = slots.cpu().numpy()
     assert_close(compare(out, oracle_step(w2), "f16"), "f16", "negative slot")
+
+
+@pytest.mark.parametrize("pt", [B.PA_PARTITION_SINGLE, 512])
+def test_decode_append_slot_inside_the_context(pt):
+    """Slots that are not the last token's: the new rows overwrite an earlier
+    position the decode reads (sequence 0: position ctx - 2; sequence 2: the
+    first token)."""
+    def make():
+        return W.custom("append_inside", "bf16", [40, 17, 300, 1], 8, 8, 128, 16, seed=14, append=True,
+                        poison=False)
+    w = make()
+    slots = w.slot_mapping.copy()
+    bs = w.block_size
+    for s_, pos in ((0, w.context_lens[0] - 2), (2, 0)):
+        slots[s_] = int(w.block_tables[s_, pos // bs]) * bs + pos % bs
+    w.slot_mapping = slots
+    g = upload(w)
+    ref_k, ref_v = g.k_cache.clone(), g.v_cache.clone()
+    B.pa_reshape_and_cache(g.new_k, g.new_v, ref_k, ref_v, g.slots, layout=g.layout)
+    out = torch.full_like(g.q, float("nan"))
+    B.pa_decode_append(out, g.q, g.new_k, g.new_v, g.k_cache, g.v_cache, g.slots, g.tables, g.ctx, w.scale,
+                       layout=g.layout, partition_tokens=pt)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(g.k_cache), _bits(ref_k)) and torch.equal(_bits(g.v_cache), _bits(ref_v))
+    assert_close(compare(out, oracle_step(w), "bf16"), "bf16", f"slots inside the context pt={pt}")
