@@ -38,9 +38,11 @@
  *     Calls only enqueue work; they never synchronise.  A call's kernels can
  *     therefore be captured in a graph on `stream` and replayed.
  *   - Every argument check runs on the host before any HIP call.  A return
- *     other than PA_OK means nothing was enqueued.  PA_ERR_HIP reports a
- *     failed launch (for example: no GPU); device faults surface at the
- *     caller's next synchronisation, as for any HIP kernel.
+ *     of PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED or PA_ERR_WORKSPACE means
+ *     nothing was enqueued.  PA_ERR_HIP reports a failed launch (for
+ *     example: no GPU); a call that enqueues several kernels and fails at a
+ *     later one leaves the kernels enqueued before it to run.  Device faults
+ *     surface at the caller's next synchronisation, as for any HIP kernel.
  *   - Elements are stored as `dtype`; all arithmetic is fp32.
  *   - 16-byte alignment is required for q, out, k, v, k_cache, v_cache and
  *     workspace (the kernels move 16-byte vectors); 4-byte alignment for the
@@ -315,8 +317,9 @@ pa_status pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_he
  *   other arguments as for pa_decode_ex; context_lens count the new token
  *
  * The append kernel is enqueued ahead of the decode, with every argument
- * checked before either: a caller that cannot check the decode's arguments
- * itself gets both steps or neither.  (Folding the append into the decode
+ * checked before either: an argument error enqueues neither step.  A launch
+ * failure of the decode (PA_ERR_HIP) comes after the append was enqueued,
+ * so the pool may already hold the new rows then.  (Folding the append into the decode
  * kernel -- the new row taken from registers where the step reads it --
  * measured no faster on MI355X: 189.9 against 190.5 us per 7B-shaped step,
  * 386.3 against 377.1 us on the mixed batch.)

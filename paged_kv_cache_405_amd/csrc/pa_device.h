@@ -176,37 +176,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr float NEG_BIG = -1.0e30f;
 
 // ---------------------------------------------------------------------------
-// A wave's window onto one block-table row.  Lane i holds entry base + i of the
-// 64-aligned window [base, base + 64) (-1 past the row's used length); entries
-// are read with v_readlane into scalar registers.  The table lookup therefore
-// never sits in the in-order vector-memory queue in front of the K/V loads: a
-// lookup costs a vector load only when the wave moves to a new window, once
-// every 64 blocks.  Block indices passed to get() must be wave-uniform.
-// ---------------------------------------------------------------------------
-struct TableWindow {
-    const int32_t *row;
-    int nblk;
-    int base;
-    int val;
-
-    __device__ __forceinline__ void init(const int32_t *r, int n) {
-        row = r;
-        nblk = n;
-        base = -64;
-        val = -1;
-    }
-    __device__ __forceinline__ int get(int j) {
-        const int b = j & ~63;
-        if (b != base) {
-            base = b;
-            const int i = b + (int)(threadIdx.x & 63);
-            val = i < nblk ? row[i] : -1;
-        }
-        return __builtin_amdgcn_readlane(val, j - b);
-    }
-};
-
-// ---------------------------------------------------------------------------
 // The tile pipeline shared by the decode workers.  A worker W provides
 //   W::Buf                          registers of one tile's K and V loads
 //   int2 W::tile_phys(int k)        physical block(s) of tile k (scalar loads)

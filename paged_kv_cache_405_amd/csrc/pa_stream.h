@@ -70,9 +70,6 @@ __device__ __forceinline__ uint64_t range_start(int w, uint64_t T, int N) {
     return q * (uint64_t)w + (r * (uint64_t)w) / (uint64_t)N;
 }
 
-#ifndef PA_STREAM_SEQ_MAJOR
-#define PA_STREAM_SEQ_MAJOR 0      // 1: units ordered sequence major (all head groups of a sequence together)
-#endif
 #ifndef PA_STREAM_XCD_MAJOR
 #define PA_STREAM_XCD_MAJOR 1      // 1: logical waves assigned XCD major
 #endif
@@ -96,8 +93,7 @@ void decode_stream_kernel(const DecodeParams P)
     // steps per head group: Tseq = sum over sequences of n(s).  Up to 64
     // sequences (one per lane) the context lengths are read once and kept:
     // the running sum that gives Tseq also locates the wave's first unit
-    constexpr bool SEQ_MAJOR = PA_STREAM_SEQ_MAJOR != 0;
-    const bool few = !SEQ_MAJOR && S <= 64;
+    const bool few = S <= 64;
     int ctx_lane = 0;              // few: lane i holds sequence i's clamped context
     int64_t incl_lane = 0, n_lane = 0;
     int64_t tseq = 0;
@@ -123,14 +119,11 @@ void decode_stream_kernel(const DecodeParams P)
     if (c_lo >= c_hi)
         return;
 
-    // locate c_lo: the sequence by a prefix scan over the units' step counts
-    // (times HG when the head groups of a sequence are consecutive), then the
-    // head group and the step
-    int hg = SEQ_MAJOR ? 0
-           : c_lo < (1ull << 32) && (uint64_t)tseq < (1ull << 32) ? (int)((uint32_t)c_lo / (uint32_t)tseq)
+    // locate c_lo: the head group, then the sequence by a prefix scan over
+    // the units' step counts, then the step
+    int hg = c_lo < (1ull << 32) && (uint64_t)tseq < (1ull << 32) ? (int)((uint32_t)c_lo / (uint32_t)tseq)
                                                                   : (int)(c_lo / (uint64_t)tseq);
     const int64_t r0 = (int64_t)(c_lo - (uint64_t)hg * (uint64_t)tseq);
-    const int64_t mult = SEQ_MAJOR ? HG : 1;
     int s = 0;
     int64_t base = 0;
     if (few) {
@@ -141,7 +134,7 @@ void decode_stream_kernel(const DecodeParams P)
     }
     for (int b = 0; b < (few ? 0 : S); b += 64) {
         const int i = b + lane;
-        const int64_t n = i < S ? mult * max(1, (clamp_ctx(P.ctx[i]) + STEP - 1) / STEP) : 0;
+        const int64_t n = i < S ? max(1, (clamp_ctx(P.ctx[i]) + STEP - 1) / STEP) : 0;
         const int64_t incl = wave_incl_scan64(n, lane);
         const int64_t tot = __shfl(incl, 63);
         if (r0 < base + tot) {
@@ -153,13 +146,7 @@ void decode_stream_kernel(const DecodeParams P)
         }
         base += uniform64(tot);
     }
-    int64_t rj = r0 - base;
-    if (SEQ_MAJOR) {
-        const int ns = max(1, (clamp_ctx(P.ctx[s]) + STEP - 1) / STEP);
-        hg = (int)(rj / ns);
-        rj -= (int64_t)hg * ns;
-    }
-    int j = __builtin_amdgcn_readfirstlane((int)rj);
+    int j = __builtin_amdgcn_readfirstlane((int)(r0 - base));
 
     W wk;
     wk.init_lane(lane);
@@ -204,12 +191,7 @@ void decode_stream_kernel(const DecodeParams P)
             break;
         first = false;
         j = 0;
-        if (SEQ_MAJOR) {
-            if (++hg == HG) {
-                hg = 0;
-                ++s;
-            }
-        } else if (++s == S) {
+        if (++s == S) {
             s = 0;
             ++hg;
         }
