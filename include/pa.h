@@ -183,6 +183,30 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, path and
+ * result as pa_decode; the split-K partials live in PA_NOALLOC_SCRATCH_BYTES
+ * of device memory the library owns, one copy per GPU, held until the process
+ * ends.  The call allocates nothing (no hipMalloc, no hipFree) and needs no
+ * zeroed memory: every kernel writes each scratch word it reads first.
+ *
+ * Every call on one GPU uses that GPU's one scratch array: calls whose work
+ * overlaps in time on the same GPU (different streams, or graphs replayed
+ * concurrently) race on it and give wrong results.  Serialise them, or use
+ * pa_decode with a workspace per stream.
+ *
+ * PA_ERR_WORKSPACE when the call would need more scratch than
+ * PA_NOALLOC_SCRATCH_BYTES (pa_decode_workspace_bytes with PA_PARTITION_AUTO
+ * gives the need); nothing is enqueued then.  Other errors as for pa_decode.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pa_status pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int block_size, int max_blocks_per_seq, float scale, pa_dtype dtype, void *stream);
+
+/*
  * pa_decode_ex -- pa_decode with the pool size, the cache layout, the
  * split-K partition and the kernel made explicit.
  *

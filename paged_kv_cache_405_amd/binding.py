@@ -5,7 +5,7 @@ pointers, the current torch stream becomes the hipStream_t.  Every step of
 the computation runs in the library's kernels.  If the library has not been
 built, loading raises ImportError -- there is no fallback path.
 
-The functions carry the C names (pa_decode, pa_decode_ex, pa_decode_path,
+The functions carry the C names (pa_decode, pa_decode_noalloc, pa_decode_ex, pa_decode_path,
 pa_decode_workspace_bytes, pa_reshape_and_cache, pa_copy_blocks,
 pa_swap_blocks, pa_status_string, pa_abi_version); `BlockManager` wraps the
 pa_bm_* calls of the host block manager.  `lib()` returns the raw ctypes
@@ -28,6 +28,7 @@ PA_LAYOUT_BHTD, PA_LAYOUT_BTHD = 0, 1
 PA_KERNEL_AUTO, PA_KERNEL_VECTOR, PA_KERNEL_MFMA = 0, 1, 2
 PA_PARTITION_AUTO, PA_PARTITION_SINGLE, PA_PARTITION_BALANCED = 0, -1, -2
 PA_DECODE_SHARED_BLOCKS = 1
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20    # scratch of pa_decode_noalloc (include/pa.h)
 STATUS_NAMES = {PA_OK: "PA_OK", PA_ERR_INVALID_ARG: "PA_ERR_INVALID_ARG", PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED",
                 PA_ERR_WORKSPACE: "PA_ERR_WORKSPACE", PA_ERR_HIP: "PA_ERR_HIP", PA_ERR_NO_BLOCKS: "PA_ERR_NO_BLOCKS"}
 POOL_GPU, POOL_CPU = 0, 1
@@ -63,6 +64,8 @@ def lib():
             vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
             L.pa_decode.restype = i32
             L.pa_decode.argtypes = [vp] * 6 + [i32] * 6 + [f32, i32, vp, sz, vp]
+            L.pa_decode_noalloc.restype = i32
+            L.pa_decode_noalloc.argtypes = [vp] * 6 + [i32] * 6 + [f32, i32, vp]
             L.pa_decode_ex.restype = i32
             L.pa_decode_ex.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, i32, i32, ctypes.c_uint32, vp, sz, vp]
             L.pa_decode_append.restype = i32
@@ -336,6 +339,21 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, *, wo
         _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode")
+    return out
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, *, stream=None):
+    """pa_decode_noalloc: pa_decode with the library's own scratch instead of a workspace (allocates nothing)."""
+    torch = _torch()
+    code = _dtype_code(q)
+    S, Hq, D = q.shape
+    NB, bs, Hkv, D2 = cache_dims(k_cache, PA_LAYOUT_BHTD)
+    st = lib().pa_decode_noalloc(
+        _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        S, Hq, Hkv, D, bs, block_tables.shape[1], float(scale), code, _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_noalloc")
     return out
 
 

@@ -208,6 +208,41 @@ int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
 
 }  // namespace
 
+// Device memory of pa_decode_noalloc: the split-K / balanced-schedule
+// workspace of a decode call, owned by the library instead of the caller.
+// Each GPU the library runs on holds its own copy until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host it names
+// a stand-in, not device memory): it passes the address hipGetSymbolAddress
+// gives for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// the address of `scratch` on the current device (looked up on the first
+// call on that device, with the device current); null on failure
+void *scratch_address()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
+}
+
+}  // namespace
+
 namespace {
 
 // The new K/V rows of a decode step: one token per sequence, sequence s's
@@ -230,7 +265,8 @@ pa_status decode_call(void *out, const void *q, const void *k_cache, const void 
                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                       int block_size, int max_blocks_per_seq, int num_blocks, float scale,
                       pa_dtype dtype, pa_layout layout, int partition_tokens, pa_kernel kernel,
-                      unsigned flags, void *workspace, size_t workspace_bytes, void *stream, const AppendRows *app)
+                      unsigned flags, void *workspace, size_t workspace_bytes, void *stream, const AppendRows *app,
+                      bool use_scratch = false)
 {
     if (flags & ~(unsigned)PA_DECODE_SHARED_BLOCKS)
         return PA_ERR_INVALID_ARG;
@@ -259,6 +295,15 @@ pa_status decode_call(void *out, const void *q, const void *k_cache, const void 
                    partition_tokens, kernel, &pl);
     if (st != PA_OK)
         return st;
+    if (use_scratch && pl.ws_bytes > 0) {
+        // the library's own scratch, once every argument has been checked
+        if (pl.ws_bytes > PA_NOALLOC_SCRATCH_BYTES)
+            return PA_ERR_WORKSPACE;
+        workspace = scratch_address();
+        if (!workspace)
+            return PA_ERR_HIP;
+        workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
+    }
     if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned(workspace, 16)))
         return PA_ERR_WORKSPACE;
 
@@ -421,6 +466,16 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
     return pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, INT32_MAX, scale, dtype,
                         PA_LAYOUT_BHTD, PA_PARTITION_AUTO, PA_KERNEL_AUTO, 0u, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int block_size, int max_blocks_per_seq, float scale, pa_dtype dtype, void *stream)
+{
+    return decode_call(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, max_blocks_per_seq, INT32_MAX, scale, dtype, PA_LAYOUT_BHTD,
+                       PA_PARTITION_AUTO, PA_KERNEL_AUTO, 0u, nullptr, 0, stream, nullptr, true);
 }
 
 }  // extern "C"
@@ -759,7 +814,7 @@ const char *pa_status_string(pa_status status)
     }
 }
 
-int pa_abi_version(void) { return 201; }
+int pa_abi_version(void) { return 202; }
 
 }  // extern "C"
 
