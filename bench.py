@@ -53,8 +53,13 @@ def parse(argv=None):
                     help="pa_decode_shared_prefix: auto = on when the workload's tables all start with the same blocks")
     ap.add_argument("--kernel", choices=["auto", "vector", "mfma"], default="auto",
                     help="decode kernel family (pa_kernel): auto picks matrix cores for grouped-query heads")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time of the headline oracle samples (the other configurations get less)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the chosen workload, not the other configurations next to it")
+    ap.add_argument("--config-steps", type=int, default=5, help="timed steps of each other configuration")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
     ap.add_argument("--op", choices=["decode", "prefill", "prefix_cache", "copy_blocks", "swap_out", "swap_in"],
                     default="decode",
                     help="decode (the default step); prefill (a 512-token chunk per sequence over a 1536-token "
@@ -372,13 +377,64 @@ def copy_calibration():
                                            "dispatches": 3}}), flush=True)
 
 
-def cpu_baseline_one_core(name, target_s):
-    """The same oracle sample on one host core: a child process with OMP_NUM_THREADS=1."""
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_sample(w, target_s, seqs_start=0):
+    """One timing of the CPU oracle (as it is) on a bounded sample of the workload: whole sequences of
+    layer 0, as many as fit in about target_s seconds.  Returns (seconds, K/V bytes, sequences)."""
+    import oracle
+    S = w.num_seqs
+    n = max(1, min(S, 4))
+    elapsed, nbytes, nseq, reps = 0.0, 0, 0, 0
+    idx = seqs_start % S
+    while elapsed < target_s and reps < 64:
+        sel = [(idx + i) % S for i in range(n)]
+        idx = (idx + n) % S
+        cl = w.context_lens[sel]
+        t0 = time.perf_counter()
+        oracle.paged_decode(w.q[sel], w.k_cache, w.v_cache, w.block_tables[sel], cl, w.scale, w.dtype)
+        dt = time.perf_counter() - t0
+        elapsed += dt
+        nbytes += int(np.sum(cl.astype(np.int64))) * w.num_kv_heads * 2 * w.head_dim * w.elem_bytes
+        nseq += n
+        reps += 1
+        if dt > 0 and elapsed < target_s:
+            n = int(min(S, max(1, n * max(1.0, (target_s - elapsed) / dt / 2))))
+    return elapsed, nbytes, nseq
+
+
+def cpu_rates(w, target_s, runs=3):
+    """The oracle's median rate over `runs` bounded samples (each about target_s seconds)."""
+    import oracle
+    samples = [cpu_sample(w, target_s, seqs_start=17 * r) for r in range(runs)]
+    gbs = [b / t / 1e9 for t, b, _ in samples]
+    sps = [n / t for t, _, n in samples]
+    return {
+        "value": round(statistics.median(gbs), 4), "unit": "GB/s",
+        "seq_layers_per_s": round(statistics.median(sps), 2),
+        "runs": runs, "values": [round(x, 4) for x in gbs],
+        "seconds": round(sum(t for t, _, _ in samples), 3),
+        "threads": oracle.num_threads(),
+        "sample": f"{sum(n for _, _, n in samples)} sequence-layers over {runs} samples",
+    }
+
+
+def cpu_baseline_one_core(name, target_s, runs=3):
+    """The same oracle samples on one host core: a child process with OMP_NUM_THREADS=1."""
     import subprocess
     code = ("import json, sys; sys.path.insert(0, %r); import bench; from paged_kv_cache_405_amd import workloads as W; "
-            "r = bench.cpu_baseline(W.WORKLOADS[%r](poison=False), %r); "
-            "print(json.dumps({k: r[k] for k in ('value', 'unit', 'cores', 'seq_layers_per_s', 'seconds')}))"
-            % (os.path.dirname(os.path.abspath(__file__)), name, float(target_s)))
+            "r = bench.cpu_rates(W.WORKLOADS[%r](poison=False), %r, %d); print(json.dumps(r))"
+            % (os.path.dirname(os.path.abspath(__file__)), name, float(target_s), runs))
     env = dict(os.environ, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
     if r.returncode != 0:
@@ -386,41 +442,28 @@ def cpu_baseline_one_core(name, target_s):
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
-def cpu_baseline(w, target_s):
-    """Time the CPU oracle (as it is) on a bounded sample of the same workload."""
-    import oracle
-    threads = oracle.num_threads()
-    S = w.num_seqs
-    # calibrate on a few sequences, then size the sample to ~target_s
-    n = max(1, min(S, 4))
-    elapsed_total, bytes_total, seqs_total, reps = 0.0, 0, 0, 0
-    idx = 0
-    while elapsed_total < target_s and reps < 64:
-        sel = [(idx + i) % S for i in range(n)]
-        idx = (idx + n) % S
-        q = w.q[sel]
-        tb = w.block_tables[sel]
-        cl = w.context_lens[sel]
-        t0 = time.perf_counter()
-        oracle.paged_decode(q, w.k_cache, w.v_cache, tb, cl, w.scale, w.dtype)
-        dt = time.perf_counter() - t0
-        elapsed_total += dt
-        bytes_total += int(np.sum(cl.astype(np.int64))) * w.num_kv_heads * 2 * w.head_dim * w.elem_bytes
-        seqs_total += n
-        reps += 1
-        if dt > 0 and elapsed_total < target_s:
-            n = int(min(S, max(1, n * max(1.0, (target_s - elapsed_total) / dt / 2))))
-    return {
-        "value": bytes_total / elapsed_total / 1e9,
-        "unit": "GB/s",
-        "cores": threads,
-        "kind": "oracle",
-        "seq_layers_per_s": seqs_total / elapsed_total,
-        "seconds": round(elapsed_total, 3),
-        "sample": (f"{seqs_total} sequence-layers of the same workload (all {w.num_q_heads} q heads each, "
-                   f"{bytes_total / 1e9:.3f} GB of K/V), fp64 oracle, {threads} OpenMP threads, "
-                   f"host cores in affinity mask: {len(os.sched_getaffinity(0))}"),
+def cpu_baseline(args, w):
+    """The CPU oracle (fp64 C, OpenMP over sequences and heads, as it is) on the GPU machine's host cores, on
+    bounded samples of the headline workload: median of 3 samples with all threads, and with one thread."""
+    t = args.cpu_seconds
+    main = cpu_rates(w, t / 3)
+    res = {
+        "value": main["value"], "unit": "GB/s", "cores": main["threads"], "kind": "oracle",
+        "sample": (f"{main['sample']} of the {w.name} workload (whole sequences, all q heads, fp64), median of "
+                   f"{main['runs']}; {main['threads']} OpenMP threads; {len(os.sched_getaffinity(0))} host cores in "
+                   f"the affinity mask; CPU: {cpu_model()}"),
+        "seq_layers_per_s": main["seq_layers_per_s"], "values": main["values"], "seconds": main["seconds"],
+        "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
     }
+    res["one_core"] = cpu_baseline_one_core(w.name, t / 6)
+    return res
+
+
+# the configurations reported next to the headline workload (the five workloads, the mixed batch at every
+# block size); each runs with its own pools, freed before the next one
+CONFIG_WORKLOADS = ["tiny_f32", "llama7b", "mixed_bs8", "mixed_bs16", "mixed_bs32", "shared_prefix",
+                    "llama70b_gqa"]
+CONFIG_POOL_BYTES = 2.5e9   # each config rotates over layers whose pools add up to at least this
 
 
 def run_config(args, w, B):
@@ -436,6 +479,208 @@ def run_config(args, w, B):
         "shared": args.shared_blocks == "on" or (args.shared_blocks == "auto" and w.shared_prefix_blocks > 0),
         # ... and can then name the prefix, read once for the whole batch
         "prefix_pass": w.shared_prefix_blocks > 0 and (args.prefix_pass == "on" or args.prefix_pass == "auto"),
+    }
+
+
+def decode_run(args, w, cfg, layers, steps, warmup, torch, B, repeats=REPEATS, warm_calls=WARM_CALLS):
+    """Time one workload: `layers` layers with their own pools; a step appends one token per sequence and
+    decodes, layer by layer.  Returns the measurements (no JSON formatting)."""
+    dev = torch.device("cuda:0")
+    layout, pt, kern, shared, dtype_code = (cfg[k] for k in ("layout", "pt", "kern", "shared", "dtype_code"))
+    prefix_pass = cfg["prefix_pass"]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+
+    def dev_arr(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # layer 0 holds the seeded workload; the other layers get their own pools
+    # and queries from a seeded device generator (same shapes, same tables)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    ctx = torch.from_numpy(w.context_lens).to(dev)
+    slots = torch.from_numpy(w.slot_mapping).to(dev)
+    kc0 = B.to_layout(dev_arr(w.k_cache), layout)
+    cache_shape = tuple(kc0.shape)
+    Ls = []
+    for li in range(layers):
+        if li == 0:
+            kc, vc = kc0, B.to_layout(dev_arr(w.v_cache), layout)
+            q, nk, nv = dev_arr(w.q), dev_arr(w.new_k), dev_arr(w.new_v)
+        else:
+            kc = torch.randn(cache_shape, generator=gen, device=dev, dtype=tdt)
+            vc = torch.randn(cache_shape, generator=gen, device=dev, dtype=tdt)
+            q = torch.randn(tuple(w.q.shape), generator=gen, device=dev, dtype=tdt)
+            nk = torch.randn(tuple(w.new_k.shape), generator=gen, device=dev, dtype=tdt)
+            nv = torch.randn(tuple(w.new_v.shape), generator=gen, device=dev, dtype=tdt)
+        Ls.append((kc, vc, q, nk, nv, torch.empty_like(q)))
+    if prefix_pass:
+        ws_bytes = B.pa_decode_shared_prefix_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                                             w.block_size, w.max_blocks_per_seq, dtype_code,
+                                                             w.shared_prefix_blocks)
+    else:
+        ws_bytes = B.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                               w.max_blocks_per_seq, dtype_code, pt)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    kv_per_layer = w.kv_bytes()
+    log(f"[bench] {w.name}: pools ready: {layers} x {2 * kc0.numel() * kc0.element_size() / 1e9:.2f} GB; "
+        f"KV bytes per decode call {kv_per_layer / 1e9:.4f} GB; workspace {ws_bytes} B")
+
+    stream = torch.cuda.current_stream()
+    # the path the library resolves the automatic choices to
+    path_pt, path_kern = B.pa_decode_path(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                          w.max_blocks_per_seq, dtype_code, pt, kern)
+    family = "mfma" if path_kern == B.PA_KERNEL_MFMA else "vec"
+    if path_pt == B.PA_PARTITION_BALANCED:
+        path_name, call_kernels = "balanced", f"decode_stream_kernel ({family}) + stream_reduce_kernel"
+    elif path_pt == B.PA_PARTITION_SINGLE:
+        path_name, call_kernels = "single", f"decode_{family}_kernel"
+    else:
+        path_name, call_kernels = f"split-K {path_pt} tokens", f"decode_{family}_kernel + reduce_kernel"
+    if prefix_pass:
+        path_name = f"shared prefix ({w.shared_prefix_blocks} blocks) once, then split-K"
+        call_kernels = f"prefix_kernel + decode_{family}_kernel (the sequences' own blocks) + reduce_kernel"
+    log(f"[bench] {w.name}: path {path_name}, kernels per call: {call_kernels}")
+
+    def decode(out, q, kc, vc):
+        if prefix_pass:
+            B.pa_decode_shared_prefix(out, q, kc, vc, tables, ctx, w.scale, w.shared_prefix_blocks, layout=layout,
+                                      workspace=ws, stream=stream)
+        else:
+            B.pa_decode_ex(out, q, kc, vc, tables, ctx, w.scale, layout=layout, partition_tokens=pt,
+                           kernel=kern, shared_blocks=shared, workspace=ws, stream=stream)
+
+    def step(events=None):
+        for li, (kc, vc, q, nk, nv, out) in enumerate(Ls):
+            B.pa_reshape_and_cache(nk, nv, kc, vc, slots, layout=layout, stream=stream)
+            if events is not None:
+                events[2 * li].record(stream)
+            decode(out, q, kc, vc)
+            if events is not None:
+                events[2 * li + 1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * layers)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(steps):
+        step(ev[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    call_ms = [ev[k][2 * li].elapsed_time(ev[k][2 * li + 1]) for k in range(steps) for li in range(layers)]
+    evented_call_ms = statistics.fmean(call_ms)
+    # the launch duration of a decode call: the same calls back to back, one
+    # event pair around all of them (an event pair per call adds its own
+    # few microseconds to every call it brackets)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for k in range(steps):
+        for kc, vc, q, nk, nv, out in Ls:
+            decode(out, q, kc, vc)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    avg_call_ms = d0.elapsed_time(d1) / (steps * layers)
+    log(f"[bench] {w.name}: {steps} steps {total_ms:.3f} ms; decode calls back to back {avg_call_ms * 1e3:.2f} us "
+        f"per call (between their own events {evented_call_ms * 1e3:.2f} us)")
+
+    def back_to_back(fn, n):
+        """Average duration of n calls of fn() issued back to back between one event pair."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def all_layers(fn):
+        return lambda: [fn(*L) for L in Ls]
+
+    # the same back-to-back pass over every layer, repeated: median and best
+    reps = [back_to_back(all_layers(lambda kc, vc, q, nk, nv, out: decode(out, q, kc, vc)), 1) / layers
+            for _ in range(repeats)]
+    # the append kernel alone, every layer once per pass
+    append_us = back_to_back(all_layers(lambda kc, vc, q, nk, nv, out: B.pa_reshape_and_cache(
+        nk, nv, kc, vc, slots, layout=layout, stream=stream)), steps) / layers
+    # warm: layer 0's pool again and again (it can then sit in the caches: not a decode step);
+    # few calls, so that a kernel trace's average over the run stays that of the real step
+    kc, vc, q, _, _, out = Ls[0]
+    warm_us = back_to_back(lambda: decode(out, q, kc, vc), warm_calls)
+    log(f"[bench] {w.name}: back-to-back passes median {statistics.median(reps):.2f} us, best {min(reps):.2f} us; "
+        f"append alone {append_us:.2f} us; warm same pool {warm_us:.2f} us")
+
+    # the bytes a call must read: every token's K and V once -- with the prefix
+    # pass, the shared prefix once for the whole batch
+    roof_bytes = kv_per_layer
+    if prefix_pass:
+        pre = w.shared_prefix_blocks * w.block_size
+        own = np.maximum(w.context_lens.astype(np.int64) - pre, 0).sum()
+        roof_bytes = int((pre + own) * w.num_kv_heads * w.head_dim * w.k_cache.dtype.itemsize * 2)
+    from paged_kv_cache_405_amd import traffic as TR
+    rec = TR.lookup(w.name, path_pt, path_kern, args.layout, shared, prefix_pass=prefix_pass)
+    del Ls, ws, kc0, kc, vc, q, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {
+        "layers": layers, "steps": steps, "warmup": warmup, "total_ms": total_ms, "avg_call_ms": avg_call_ms,
+        "evented_call_ms": evented_call_ms, "reps": reps, "append_us": append_us, "warm_us": warm_us,
+        "path_name": path_name, "call_kernels": call_kernels, "family": family, "kv_per_layer": kv_per_layer,
+        "roof_bytes": roof_bytes, "traffic_record": rec,
+    }
+
+
+def stream_probe(torch, B, nbytes=8 << 30, reps=3):
+    """The streaming-read probe (pa_probe_stream_read) on an 8 GiB buffer: the best read rate over a few
+    workgroup counts and both access modes, each timed back to back (reps launches between one event
+    pair).  Context for the HBM fraction of the decode kernels; the roofline's peak stays 8 TB/s."""
+    dev = torch.device("cuda:0")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    results = []
+    for mode, wgs in ((0, 1024), (0, 2048), (0, 4096), (0, 8192), (1, 2048), (1, 8192)):
+        B.pa_probe_stream_read(buf, sink, wgs, mode, stream=stream)          # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            B.pa_probe_stream_read(buf, sink, wgs, mode, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        results.append({"mode": "contiguous chunk per workgroup" if mode == 0 else "grid stride",
+                        "workgroups": wgs, "us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    del buf, sink
+    torch.cuda.empty_cache()
+    best = max(results, key=lambda r: r["gbs"])
+    log(f"[bench] streaming-read probe: best {best['gbs']} GB/s ({best['mode']}, {best['workgroups']} workgroups)")
+    return best, results
+
+
+def config_entry(w, m, traffic_ok=True):
+    """The measurements of one workload as a JSON object."""
+    achieved = m["roof_bytes"] / (m["avg_call_ms"] * 1e-3) / 1e9
+    calls = m["steps"] * m["layers"]
+    rec = m["traffic_record"]
+    return {
+        "workload": f"{w.name}: {w.description}", "dtype": w.dtype, "layers": m["layers"], "steps": m["steps"],
+        "path": m["path_name"], "kernels": m["call_kernels"],
+        "call_us": round(m["avg_call_ms"] * 1e3, 3),
+        "call_us_repeats_median": round(statistics.median(m["reps"]), 3),
+        "bytes_per_call": m["roof_bytes"], "achieved_gbs": round(achieved, 2),
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": None if rec is None or not traffic_ok else int(round(rec["bytes_per_call"])),
+        "seq_layers_per_s": round(w.num_seqs * calls / (m["total_ms"] * 1e-3), 1),
+        "append_and_decode_us_per_layer": round(m["total_ms"] * 1e3 / calls, 3),
+        "kv_gbs_step": round(m["kv_per_layer"] * calls / (m["total_ms"] * 1e-3) / 1e9, 2),
     }
 
 
@@ -471,163 +716,14 @@ def main():
 
     w = W.WORKLOADS[args.workload](poison=False)
     cfg = run_config(args, w, B)
-    layers, layout, pt, kern, shared, dtype_code = (cfg[k] for k in ("layers", "layout", "pt", "kern", "shared",
-                                                                        "dtype_code"))
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
-    log(f"[bench] workload {w.name}: {w.description}; layers {layers}; partition {pt}; layout {args.layout}")
-
-    def dev_arr(a):
-        if w.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    # layer 0 holds the seeded workload; the other layers get their own pools
-    # and queries from a seeded device generator (same shapes, same tables)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(1234)
-    tables = torch.from_numpy(w.block_tables).to(dev)
-    ctx = torch.from_numpy(w.context_lens).to(dev)
-    slots = torch.from_numpy(w.slot_mapping).to(dev)
-    kc0 = B.to_layout(dev_arr(w.k_cache), layout)
-    cache_shape = tuple(kc0.shape)
-    Ls = []
-    for li in range(layers):
-        if li == 0:
-            kc, vc = kc0, B.to_layout(dev_arr(w.v_cache), layout)
-            q, nk, nv = dev_arr(w.q), dev_arr(w.new_k), dev_arr(w.new_v)
-        else:
-            kc = torch.randn(cache_shape, generator=gen, device=dev, dtype=tdt)
-            vc = torch.randn(cache_shape, generator=gen, device=dev, dtype=tdt)
-            q = torch.randn(tuple(w.q.shape), generator=gen, device=dev, dtype=tdt)
-            nk = torch.randn(tuple(w.new_k.shape), generator=gen, device=dev, dtype=tdt)
-            nv = torch.randn(tuple(w.new_v.shape), generator=gen, device=dev, dtype=tdt)
-        Ls.append((kc, vc, q, nk, nv, torch.empty_like(q)))
-    prefix_pass = cfg["prefix_pass"]
-    if prefix_pass:
-        ws_bytes = B.pa_decode_shared_prefix_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                                             w.block_size, w.max_blocks_per_seq, dtype_code,
-                                                             w.shared_prefix_blocks)
-    else:
-        ws_bytes = B.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
-                                               w.max_blocks_per_seq, dtype_code, pt)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    kv_per_layer = w.kv_bytes()
-    log(f"[bench] pools ready: {layers} x {2 * kc0.numel() * kc0.element_size() / 1e9:.2f} GB; "
-        f"KV bytes per decode call {kv_per_layer / 1e9:.4f} GB; workspace {ws_bytes} B")
-
-    stream = torch.cuda.current_stream()
-    # the path the library resolves the automatic choices to
-    path_pt, path_kern = B.pa_decode_path(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
-                                          w.max_blocks_per_seq, dtype_code, pt, kern)
-    family = "mfma" if path_kern == B.PA_KERNEL_MFMA else "vec"
-    if path_pt == B.PA_PARTITION_BALANCED:
-        path_name, call_kernels = "balanced", f"decode_stream_kernel ({family}) + stream_reduce_kernel"
-    elif path_pt == B.PA_PARTITION_SINGLE:
-        path_name, call_kernels = "single", f"decode_{family}_kernel"
-    else:
-        path_name, call_kernels = f"split-K {path_pt} tokens", f"decode_{family}_kernel + reduce_kernel"
-    if prefix_pass:
-        path_name = f"shared prefix ({w.shared_prefix_blocks} blocks) once, then split-K"
-        call_kernels = f"prefix_kernel + decode_{family}_kernel (the sequences' own blocks) + reduce_kernel"
-    log(f"[bench] path: {path_name}, kernels per call: {call_kernels}")
-
-    def decode(out, q, kc, vc):
-        if prefix_pass:
-            B.pa_decode_shared_prefix(out, q, kc, vc, tables, ctx, w.scale, w.shared_prefix_blocks, layout=layout,
-                                      workspace=ws, stream=stream)
-        else:
-            B.pa_decode_ex(out, q, kc, vc, tables, ctx, w.scale, layout=layout, partition_tokens=pt,
-                           kernel=kern, shared_blocks=shared, workspace=ws, stream=stream)
-
-    def step(events=None):
-        for li, (kc, vc, q, nk, nv, out) in enumerate(Ls):
-            B.pa_reshape_and_cache(nk, nv, kc, vc, slots, layout=layout, stream=stream)
-            if events is not None:
-                events[2 * li].record(stream)
-            decode(out, q, kc, vc)
-            if events is not None:
-                events[2 * li + 1].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * layers)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for k in range(args.steps):
-        step(ev[k])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    call_ms = [ev[k][2 * li].elapsed_time(ev[k][2 * li + 1]) for k in range(args.steps) for li in range(layers)]
-    avg_call_ms = statistics.fmean(call_ms)
-    log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms (wall {wall * 1e3:.3f} ms); "
-        f"decode call between its own events avg {avg_call_ms * 1e3:.2f} us, "
-        f"median {statistics.median(call_ms) * 1e3:.2f} us")
-    # the launch duration of a decode call: the same calls back to back, one
-    # event pair around all of them (an event pair per call adds its own
-    # few microseconds to every call it brackets)
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for k in range(args.steps):
-        for kc, vc, q, nk, nv, out in Ls:
-            decode(out, q, kc, vc)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    evented_call_ms = avg_call_ms
-    avg_call_ms = d0.elapsed_time(d1) / (args.steps * layers)
-    log(f"[bench] decode calls back to back: {avg_call_ms * 1e3:.2f} us per call")
-
-    def back_to_back(fn, n):
-        """Average duration of n calls of fn() issued back to back between one event pair."""
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / n
-
-    def all_layers(fn):
-        return lambda: [fn(*L) for L in Ls]
-
-    # the same back-to-back pass over every layer, repeated: median and best
-    reps = [back_to_back(all_layers(lambda kc, vc, q, nk, nv, out: decode(out, q, kc, vc)), 1) / layers
-            for _ in range(REPEATS)]
-    # the append kernel alone, every layer once per pass
-    append_us = back_to_back(all_layers(lambda kc, vc, q, nk, nv, out: B.pa_reshape_and_cache(
-        nk, nv, kc, vc, slots, layout=layout, stream=stream)), args.steps) / layers
-    # warm: layer 0's pool again and again (it can then sit in the caches: not a decode step);
-    # few calls, so that a kernel trace's average over the run stays that of the real step
-    kc, vc, q, _, _, out = Ls[0]
-    warm_us = back_to_back(lambda: decode(out, q, kc, vc), WARM_CALLS)
-    log(f"[bench] back-to-back passes: median {statistics.median(reps):.2f} us, best {min(reps):.2f} us per call; "
-        f"append alone {append_us:.2f} us; warm same pool {warm_us:.2f} us")
-
-    # HBM bytes per call from the committed counter record, when it was taken
-    # on these kernel sources (else null)
-    from paged_kv_cache_405_amd import traffic as TR
-    rec = None if prefix_pass else TR.lookup(args.workload, path_pt, path_kern, args.layout, shared)
-    traffic_bytes = None if rec is None else int(round(rec["bytes_per_call"]))
-    traffic_source = None if rec is None else "profiles/hbm_traffic.json (rocprofv3 FETCH_SIZE, WRITE_SIZE)"
-    calls = args.steps * layers
-    kv_gbs = kv_per_layer * calls / (total_ms * 1e-3) / 1e9
-    # the bytes a call must read: every token's K and V once -- with the prefix
-    # pass, the shared prefix once for the whole batch
-    roof_bytes = kv_per_layer
-    if prefix_pass:
-        pre = w.shared_prefix_blocks * w.block_size
-        own = np.maximum(w.context_lens.astype(np.int64) - pre, 0).sum()
-        roof_bytes = int((pre + own) * w.num_kv_heads * w.head_dim * w.k_cache.dtype.itemsize * 2)
-    achieved = roof_bytes / (avg_call_ms * 1e-3) / 1e9
-    seq_layers = w.num_seqs * calls / (total_ms * 1e-3)
+    log(f"[bench] workload {w.name}: {w.description}; layers {cfg['layers']}; partition {cfg['pt']}; "
+        f"layout {args.layout}")
+    m = decode_run(args, w, cfg, cfg["layers"], args.steps, args.warmup, torch, B)
+    calls = args.steps * m["layers"]
+    total_ms, avg_call_ms = m["total_ms"], m["avg_call_ms"]
+    kv_gbs = m["kv_per_layer"] * calls / (total_ms * 1e-3) / 1e9
+    achieved = m["roof_bytes"] / (avg_call_ms * 1e-3) / 1e9
+    rec = m["traffic_record"]
     result = {
         "metric": METRIC,
         "value": round(kv_gbs, 2),
@@ -644,39 +740,62 @@ def main():
         "config": {
             "workload": f"{w.name}: {w.description}",
             "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
-            "head_dim": w.head_dim, "block_size": w.block_size, "layers": layers,
-            "partition_tokens": pt, "layout": args.layout, "kernel": args.kernel,
-            "path": {"partition": path_name, "kernel_family": family},
-            "shared_blocks": shared, "prefix_pass": prefix_pass, "sum_context_tokens": int(w.context_lens.sum()),
-            "parallelism": "single GPU",
+            "head_dim": w.head_dim, "block_size": w.block_size, "layers": m["layers"],
+            "partition_tokens": cfg["pt"], "layout": args.layout, "kernel": args.kernel,
+            "path": {"partition": m["path_name"], "kernel_family": m["family"]},
+            "shared_blocks": cfg["shared"], "prefix_pass": cfg["prefix_pass"],
+            "sum_context_tokens": int(w.context_lens.sum()), "parallelism": "single GPU",
         },
-        "seq_layers_per_s": round(seq_layers, 1),
+        "seq_layers_per_s": round(w.num_seqs * calls / (total_ms * 1e-3), 1),
         "hbm_peak_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
-        "kv_bytes_per_layer": kv_per_layer,
+        "kv_bytes_per_layer": m["kv_per_layer"],
         "roofline": {
-            "kernel": f"pa_decode call: {call_kernels}",
+            "kernel": f"pa_decode call: {m['call_kernels']}",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_bytes,
-            "traffic_source": traffic_source,
+            "traffic": None if rec is None else int(round(rec["bytes_per_call"])),
+            "traffic_source": None if rec is None else "profiles/hbm_traffic.json (rocprofv3 FETCH_SIZE, WRITE_SIZE)",
             "avg_call_us": round(avg_call_ms * 1e3, 3),
-            "avg_call_us_own_events": round(evented_call_ms * 1e3, 3),
-            "bytes_per_call": roof_bytes,
+            "avg_call_us_own_events": round(m["evented_call_ms"] * 1e3, 3),
+            "bytes_per_call": m["roof_bytes"],
         },
         "append_and_decode_us_per_layer": round(total_ms * 1e3 / calls, 3),
-        "append_us": round(append_us, 3),
-        "call_us_repeats": {"n": REPEATS, "median": round(statistics.median(reps), 3), "best": round(min(reps), 3),
+        "append_us": round(m["append_us"], 3),
+        "call_us_repeats": {"n": REPEATS, "median": round(statistics.median(m["reps"]), 3),
+                            "best": round(min(m["reps"]), 3),
                             "what": "all layers' decode calls back to back, one event pair per pass"},
-        "warm_same_pool_call_us": round(warm_us, 3),
+        "warm_same_pool_call_us": round(m["warm_us"], 3),
     }
+    if not args.no_probe:
+        best, allp = stream_probe(torch, B)
+        result["roofline"]["stream_probe_gbs"] = best["gbs"]
+        result["roofline"]["stream_probe"] = {"best": best, "all": allp,
+                                              "what": "pa_probe_stream_read over 8 GiB, non-temporal 16-byte loads"}
+    if not args.no_configs:
+        # the other configurations, each with its own pools (freed before the next)
+        configs = {}
+        for name in CONFIG_WORKLOADS:
+            if name == w.name:
+                continue
+            cw = W.WORKLOADS[name](poison=False)
+            ccfg = run_config(args, cw, B)
+            pool = 2 * cw.k_cache.nbytes
+            layers = max(4, min(ccfg["layers"], int(np.ceil(CONFIG_POOL_BYTES / max(pool, 1)))))
+            cm = decode_run(args, cw, ccfg, layers, args.config_steps, 2, torch, B, repeats=3, warm_calls=5)
+            configs[name] = config_entry(cw, cm)
+            if not args.no_cpu_baseline:
+                # the oracle on the same workload: median of 3 shorter samples, all threads
+                r = cpu_rates(cw, args.cpu_seconds / 8)
+                configs[name]["cpu_baseline"] = {k: r[k] for k in ("value", "unit", "seq_layers_per_s", "values",
+                                                                   "seconds", "threads")}
+            del cw
+        result["configs"] = configs
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        cw = W.WORKLOADS[args.workload](poison=False)
-        result["cpu_baseline"] = cpu_baseline(cw, args.cpu_seconds)
-        result["cpu_baseline"]["one_core"] = cpu_baseline_one_core(args.workload, args.cpu_seconds)
+        log("[bench] timing the CPU oracle on bounded samples")
+        result["cpu_baseline"] = cpu_baseline(args, w)
     print(json.dumps(result), flush=True)
 
 

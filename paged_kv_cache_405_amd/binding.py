@@ -120,6 +120,8 @@ def lib():
             L.pa_prefill.restype = i32
             L.pa_prefill.argtypes = [vp] * 7 + [i32] * 9 + [f32, i32, i32, ctypes.c_uint32, vp]
             L.pa_status_string.restype = ctypes.c_char_p
+            L.pa_probe_stream_read.restype = i32
+            L.pa_probe_stream_read.argtypes = [vp, sz, vp, i32, i32, vp]
             L.pa_status_string.argtypes = [i32]
             L.pa_abi_version.restype = i32
             L.pa_abi_version.argtypes = []
@@ -373,6 +375,16 @@ def pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, layout=PA_LAYO
     if st != PA_OK:
         raise PaError(st, "pa_reshape_and_cache")
     return k_cache, v_cache
+
+
+def pa_probe_stream_read(buf, sink, workgroups: int, mode: int = 0, *, stream=None):
+    """Read the whole of `buf` (a device tensor) once; sink (uint32/int32, >= workgroups) gets one XOR per workgroup."""
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_cuda or sink.numel() < workgroups:
+        raise ValueError("buf and sink must be contiguous device tensors, sink holding one word per workgroup")
+    st = lib().pa_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                    int(workgroups), int(mode), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_probe_stream_read")
 
 
 def to_layout(cache_bthd, layout: int):

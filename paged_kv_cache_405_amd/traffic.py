@@ -10,7 +10,7 @@ and build flags: once they change, the measurement no longer describes the
 code and ``lookup`` returns None.
 
     python -m paged_kv_cache_405_amd.traffic record --workload llama7b \\
-        --partition -1 --kernel 1 --layout bhtd [--shared-blocks] \\
+        --partition -1 --kernel 1 --layout bhtd [--shared-blocks] [--prefix-pass] \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --command "rocprofv3 ..." [--command ...]
 
@@ -70,11 +70,12 @@ def _copy_kib(dirname: str, counter: str) -> float:
 
 
 def _key(r):
-    return (r["workload"], r["partition"], r["kernel"], r["layout"], r.get("shared_blocks", False))
+    return (r["workload"], r["partition"], r["kernel"], r["layout"], r.get("shared_blocks", False),
+            r.get("prefix_pass", False))
 
 
 def record(path, workload, partition, kernel, layout, shared_blocks, fetch_dir, write_dir, copy_fetch_dir,
-           copy_write_dir, commands):
+           copy_write_dir, commands, prefix_pass=False):
     fetch = _decode_kernels(_counter(fetch_dir, "FETCH_SIZE"))
     write = _decode_kernels(_counter(write_dir, "WRITE_SIZE"))
     fetch_scale = COPY_BYTES / 1024 / _copy_kib(copy_fetch_dir, "FETCH_SIZE")
@@ -86,7 +87,7 @@ def record(path, workload, partition, kernel, layout, shared_blocks, fetch_dir, 
     write_bytes = sum(v["WRITE_SIZE_kib"] for v in kernels.values()) * 1024 * write_scale
     entry = {
         "workload": workload, "partition": int(partition), "kernel": int(kernel), "layout": layout,
-        "shared_blocks": bool(shared_blocks),
+        "shared_blocks": bool(shared_blocks), "prefix_pass": bool(prefix_pass),
         "sources_sha256": sources_digest(),
         "fetch_scale": fetch_scale, "write_scale": write_scale,
         "kernels": kernels,
@@ -105,7 +106,7 @@ def record(path, workload, partition, kernel, layout, shared_blocks, fetch_dir, 
     return entry
 
 
-def lookup(workload, partition, kernel, layout, shared_blocks=False, path=DEFAULT_PATH):
+def lookup(workload, partition, kernel, layout, shared_blocks=False, path=DEFAULT_PATH, prefix_pass=False):
     """The record for this configuration if it was measured on the current sources, else None."""
     if not os.path.exists(path):
         return None
@@ -113,7 +114,7 @@ def lookup(workload, partition, kernel, layout, shared_blocks=False, path=DEFAUL
         data = json.load(fh)
     digest = sources_digest()
     for r in data.get("records", []):
-        if _key(r) == (workload, partition, kernel, layout, bool(shared_blocks)):
+        if _key(r) == (workload, partition, kernel, layout, bool(shared_blocks), bool(prefix_pass)):
             return r if r["sources_sha256"] == digest else None
     return None
 
@@ -128,6 +129,7 @@ def main():
     r.add_argument("--kernel", type=int, required=True)
     r.add_argument("--layout", default="bhtd")
     r.add_argument("--shared-blocks", action="store_true")
+    r.add_argument("--prefix-pass", action="store_true", help="the call was pa_decode_shared_prefix")
     r.add_argument("--fetch", required=True)
     r.add_argument("--write", required=True)
     r.add_argument("--copy-fetch", required=True)
@@ -135,7 +137,7 @@ def main():
     r.add_argument("--command", action="append", default=[])
     a = ap.parse_args()
     e = record(a.path, a.workload, a.partition, a.kernel, a.layout, a.shared_blocks, a.fetch, a.write,
-               a.copy_fetch, a.copy_write, a.command)
+               a.copy_fetch, a.copy_write, a.command, prefix_pass=a.prefix_pass)
     print(json.dumps({k: e[k] for k in ("workload", "partition", "kernel", "bytes_per_call", "read_bytes_per_call",
                                         "write_bytes_per_call", "fetch_scale", "write_scale")}))
 

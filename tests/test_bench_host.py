@@ -56,3 +56,19 @@ def test_flags_and_overrides(made):
 
 def test_default_workload_is_the_7b_shape():
     assert bench.parse([]).workload == "llama7b"
+
+
+def test_cpu_rates_on_a_small_workload():
+    """the oracle timing helper: median of its samples, positive rates, the thread count it used"""
+    w = W.tiny_f32(poison=False)
+    r = bench.cpu_rates(w, 0.05, runs=3)
+    assert r["runs"] == 3 and len(r["values"]) == 3 and r["value"] == sorted(r["values"])[1]
+    assert r["value"] > 0 and r["seq_layers_per_s"] > 0 and r["threads"] >= 1
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_config_list_covers_the_five_workloads():
+    assert {"tiny_f32", "llama7b", "mixed_bs8", "mixed_bs16", "mixed_bs32", "shared_prefix",
+            "llama70b_gqa"} <= set(bench.CONFIG_WORKLOADS)
+    a = bench.parse(["--no-configs", "--no-probe", "--config-steps", "2"])
+    assert a.no_configs and a.no_probe and a.config_steps == 2
