@@ -42,7 +42,7 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "llama70b_gqa", "llama70b_tp8", "mixed_bs8", "mixed_bs16", "mixed_bs32",
-                             "shared_prefix"])
+                             "shared_prefix", "tiny_f32"])
     ap.add_argument("--layers", type=int, default=None, help="default: 32 (7B-shaped), 80 (70B-shaped)")
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="0 = library's choice (default), -1 = single pass, -2 = balanced schedule, N = split-K partition of N tokens")

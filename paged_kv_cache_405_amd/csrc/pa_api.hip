@@ -49,6 +49,18 @@ constexpr long long AUTO_UNITS_PER_CU = 4;   // single pass at or above this man
 // 69.2 us without)
 constexpr long long ORDER_ROWS_MIN_TOKENS = 512;
 
+// Tokens per step of the vector worker (its schedule unit): one or two
+// wave-wide loads of 64 / (head_dim * elem_bytes / 16) token rows each, as
+// many as a block holds.  Mirrors VecWorker's STEP_TOK.
+long long vec_step_tokens(pa_dtype dtype, int head_dim, int block_size)
+{
+    const int vec = dtype == PA_F32 ? 4 : 8;           // elements per 16 bytes
+    const int rows_per_load = 64 / (head_dim / vec);
+    const int rows = rows_per_load < block_size ? rows_per_load : block_size;
+    const int loads_per_block = block_size / rows;
+    return (long long)(loads_per_block < 2 ? loads_per_block : 2) * rows;
+}
+
 struct Plan {
     bool mfma = false;          // grouped-query matrix-core kernel
     bool stream = false;        // balanced schedule (partition_tokens == 0)
@@ -164,6 +176,13 @@ pa_status make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_di
         if (occ <= 0)
             return PA_ERR_HIP;
         long long waves = (long long)cus * occ / 8 * 8;
+        // never more waves than the stream can hold steps: a small batch
+        // would otherwise start thousands of workgroups that find their
+        // range empty (the tiny workload: 18 steps at most, 8192 waves)
+        const long long step_tok = pl->mfma ? 16 : vec_step_tokens(dtype, head_dim, block_size);
+        const long long max_steps = (long long)num_seqs * num_kv_heads * pl->group_split *
+                                    (((long long)max_blocks_per_seq * block_size + step_tok - 1) / step_tok);
+        waves = std::min(waves, (max_steps + 7) / 8 * 8);
         waves = waves < 8 ? 8 : (waves > (1 << 16) ? (1 << 16) : waves);   // N <= 2^16: 32-bit range arithmetic
         pl->stream = true;
         pl->n_waves = (int)waves;
