@@ -65,13 +65,21 @@ typedef enum pa_status {
     PA_ERR_UNSUPPORTED = 2,   /* head_dim, block_size, dtype, layout or kernel outside the supported set */
     PA_ERR_WORKSPACE = 3,     /* split-K needs a workspace and the one given is missing or too small */
     PA_ERR_HIP = 4,           /* a HIP launch failed */
-    PA_ERR_NO_BLOCKS = 5      /* pa_blocks.h: not enough free blocks; nothing was changed */
+    PA_ERR_NO_BLOCKS = 5,     /* pa_blocks.h: not enough free blocks; nothing was changed */
+    /* not values: they give the type the range of a 32-bit int, so that any
+       int a C caller passes is a valid value of it and reaches the checks */
+    PA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    PA_STATUS_RANGE_MAX_ = 2147483647
 } pa_status;
 
 typedef enum pa_dtype {
     PA_F32 = 0,
     PA_F16 = 1,
-    PA_BF16 = 2
+    PA_BF16 = 2,
+    /* not values: they give the type the range of a 32-bit int, so that any
+       int a C caller passes is a valid value of it and reaches the checks */
+    PA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    PA_DTYPE_RANGE_MAX_ = 2147483647
 } pa_dtype;
 
 /*
@@ -85,7 +93,11 @@ typedef enum pa_dtype {
  */
 typedef enum pa_layout {
     PA_LAYOUT_BHTD = 0,
-    PA_LAYOUT_BTHD = 1
+    PA_LAYOUT_BTHD = 1,
+    /* not values: they give the type the range of a 32-bit int, so that any
+       int a C caller passes is a valid value of it and reaches the checks */
+    PA_LAYOUT_RANGE_MIN_ = -2147483647 - 1,
+    PA_LAYOUT_RANGE_MAX_ = 2147483647
 } pa_layout;
 
 /*
@@ -105,7 +117,11 @@ typedef enum pa_layout {
 typedef enum pa_kernel {
     PA_KERNEL_AUTO = 0,
     PA_KERNEL_VECTOR = 1,
-    PA_KERNEL_MFMA = 2
+    PA_KERNEL_MFMA = 2,
+    /* not values: they give the type the range of a 32-bit int, so that any
+       int a C caller passes is a valid value of it and reaches the checks */
+    PA_KERNEL_RANGE_MIN_ = -2147483647 - 1,
+    PA_KERNEL_RANGE_MAX_ = 2147483647
 } pa_kernel;
 
 /*
