@@ -640,14 +640,15 @@ def decode_run(args, w, cfg, layers, steps, warmup, torch, B, repeats=REPEATS, w
 
 def stream_probe(torch, B, nbytes=8 << 30, reps=3):
     """The streaming-read probe (pa_probe_stream_read) on an 8 GiB buffer: the best read rate over a few
-    workgroup counts and both access modes, each timed back to back (reps launches between one event
-    pair).  Context for the HBM fraction of the decode kernels; the roofline's peak stays 8 TB/s."""
+    workgroup counts of the contiguous and grid-stride modes, and the rate of the scattered 4 KiB block mode
+    (a paged pool's access pattern), each timed back to back (reps launches between one event pair).
+    Context for the HBM fraction of the decode kernels; the roofline's peak stays 8 TB/s."""
     dev = torch.device("cuda:0")
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     results = []
-    for mode, wgs in ((0, 1024), (0, 2048), (0, 4096), (0, 8192), (1, 2048), (1, 8192)):
+    for mode, wgs in ((0, 1024), (0, 2048), (0, 4096), (0, 8192), (1, 2048), (1, 8192), (2, 2048), (2, 8192)):
         B.pa_probe_stream_read(buf, sink, wgs, mode, stream=stream)          # warm-up
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -656,11 +657,11 @@ def stream_probe(torch, B, nbytes=8 << 30, reps=3):
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
-        results.append({"mode": "contiguous chunk per workgroup" if mode == 0 else "grid stride",
+        results.append({"mode": ["contiguous chunk per workgroup", "grid stride", "scattered 4 KiB blocks"][mode],
                         "workgroups": wgs, "us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
     del buf, sink
     torch.cuda.empty_cache()
-    best = max(results, key=lambda r: r["gbs"])
+    best = max((r for r in results if r["mode"] != "scattered 4 KiB blocks"), key=lambda r: r["gbs"])
     log(f"[bench] streaming-read probe: best {best['gbs']} GB/s ({best['mode']}, {best['workgroups']} workgroups)")
     return best, results
 
@@ -772,6 +773,7 @@ def main():
     if not args.no_probe:
         best, allp = stream_probe(torch, B)
         result["roofline"]["stream_probe_gbs"] = best["gbs"]
+        result["roofline"]["scattered_4k_probe_gbs"] = max(r["gbs"] for r in allp if r["mode"] == "scattered 4 KiB blocks")
         result["roofline"]["stream_probe"] = {"best": best, "all": allp,
                                               "what": "pa_probe_stream_read over 8 GiB, non-temporal 16-byte loads"}
     if not args.no_configs:

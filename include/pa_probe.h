@@ -33,7 +33,10 @@ extern "C" {
  *   workgroups  1 .. 2^20 workgroups of 256 threads
  *   mode        0: each workgroup reads one contiguous 1/workgroups share of
  *               the buffer; 1: the workgroups stride through the buffer in
- *               32 KiB steps (grid stride)
+ *               32 KiB steps (grid stride); 2: the buffer is read as 4 KiB
+ *               blocks in a scattered order (logical block i is physical block
+ *               i * 0x9E3779B1 modulo the block count), the access pattern of
+ *               a paged pool -- bytes must then be 4 KiB times a power of two
  *
  * Enqueued on `stream`; time it with events around the call.  Errors:
  * PA_ERR_INVALID_ARG (null or misaligned pointer, size, count or mode out of

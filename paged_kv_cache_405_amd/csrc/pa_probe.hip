@@ -14,7 +14,13 @@
 //   mode 0: workgroup b reads one contiguous chunk, the b-th of `workgroups`
 //           equal chunks of the buffer;
 //   mode 1: grid stride: iteration i of workgroup b reads the 32 KiB step
-//           i * workgroups + b of the buffer.
+//           i * workgroups + b of the buffer;
+//   mode 2: the buffer as 4 KiB blocks (a power-of-two count of them) read in
+//           a scattered order -- logical block i is physical block
+//           (i * 0x9E3779B1) mod count, a bijection -- and each workgroup
+//           takes one contiguous 1/workgroups share of the logical blocks:
+//           the access pattern of a paged K/V pool (one 4 KiB (block, head)
+//           tile at a time, wherever the block manager placed it).
 #include "pa_device.h"
 #include "pa_probe.h"
 
@@ -49,6 +55,26 @@ __global__ __launch_bounds__(PROBE_THREADS) void stream_read_kernel(const pa_u32
         }
         for (uint64_t j = i + t; j < hi; j += PROBE_THREADS)
             x ^= fold(__builtin_nontemporal_load(src + j));
+    } else if (mode == 2) {
+        constexpr uint64_t BLK = 4096 / 16;                         // words per block: one per thread
+        const uint64_t nblk = n16 / BLK;
+        const uint64_t per = (nblk + nwg - 1) / nwg;
+        const uint64_t lo = b * per;
+        const uint64_t hi = lo + per < nblk ? lo + per : nblk;
+        uint64_t i = lo;
+        for (; i + PROBE_UNROLL <= hi; i += PROBE_UNROLL) {
+            pa_u32x4 v[PROBE_UNROLL];
+#pragma unroll
+            for (int u = 0; u < PROBE_UNROLL; ++u) {
+                const uint64_t phys = ((i + u) * 0x9E3779B1ull) & (nblk - 1);
+                v[u] = __builtin_nontemporal_load(src + phys * BLK + t);
+            }
+#pragma unroll
+            for (int u = 0; u < PROBE_UNROLL; ++u)
+                x ^= fold(v[u]);
+        }
+        for (; i < hi; ++i)
+            x ^= fold(__builtin_nontemporal_load(src + ((i * 0x9E3779B1ull) & (nblk - 1)) * BLK + t));
     } else {
         uint64_t i = b * STEP;
         for (; i + STEP <= n16; i += nwg * STEP) {
@@ -90,7 +116,10 @@ extern "C" pa_status pa_probe_stream_read(const void *src, size_t bytes, uint32_
         return PA_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3) != 0)
         return PA_ERR_INVALID_ARG;
-    if (mode != 0 && mode != 1)
+    if (mode != 0 && mode != 1 && mode != 2)
+        return PA_ERR_INVALID_ARG;
+    // mode 2: a power-of-two number of 4 KiB blocks
+    if (mode == 2 && (bytes % 4096 != 0 || ((bytes / 4096) & (bytes / 4096 - 1)) != 0))
         return PA_ERR_INVALID_ARG;
     hipLaunchKernelGGL(pa::stream_read_kernel, dim3(workgroups), dim3(pa::PROBE_THREADS), 0,
                        static_cast<hipStream_t>(stream), static_cast<const pa::pa_u32x4 *>(src),

@@ -147,7 +147,8 @@ int main()
     EXPECT(pa_copy_blocks(F, F, I(F), 0, 8, 16, 2, 64, PA_F16, nullptr), PA_OK);
     EXPECT(pa_probe_stream_read(F, 100, static_cast<uint32_t *>(F), 4, 0, nullptr), PA_ERR_INVALID_ARG);
     EXPECT(pa_probe_stream_read(F, 1 << 20, static_cast<uint32_t *>(F), 0, 0, nullptr), PA_ERR_INVALID_ARG);
-    EXPECT(pa_probe_stream_read(F, 1 << 20, static_cast<uint32_t *>(F), 4, 2, nullptr), PA_ERR_INVALID_ARG);
+    EXPECT(pa_probe_stream_read(F, 1 << 20, static_cast<uint32_t *>(F), 4, 3, nullptr), PA_ERR_INVALID_ARG);
+    EXPECT(pa_probe_stream_read(F, 3 * 4096, static_cast<uint32_t *>(F), 4, 2, nullptr), PA_ERR_INVALID_ARG);
     // status strings and version
     for (int s = -1; s <= 6; ++s)
         if (!pa_status_string((pa_status)s) || !pa_status_string((pa_status)s)[0])
