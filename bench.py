@@ -463,7 +463,7 @@ def cpu_baseline(args, w):
 # block size); each runs with its own pools, freed before the next one
 CONFIG_WORKLOADS = ["tiny_f32", "llama7b", "mixed_bs8", "mixed_bs16", "mixed_bs32", "shared_prefix",
                     "llama70b_gqa"]
-CONFIG_POOL_BYTES = 2.5e9   # each config rotates over layers whose pools add up to at least this
+CONFIG_POOL_BYTES = 40e9    # each config rotates over its model's layers, as many as fit in this many bytes of pools
 
 
 def run_config(args, w, B):

@@ -25,8 +25,8 @@
 
 namespace pa {
 
-// One workgroup of PF_WAVES waves per (group of PF_WAVES column tiles, head
-// group, sequence): wave i owns column tile PF_WAVES * g + i and sees every
+// One workgroup of NW waves per (group of NW column tiles, head group,
+// sequence): wave i owns column tile NW * g + i and sees every
 // key tile its columns attend.  A key tile goes from memory into LDS once for
 // the whole workgroup -- its K and V moved by direct-to-LDS loads that the
 // waves share out -- and every wave reads it there:
@@ -51,15 +51,19 @@ namespace pa {
 // Logical workgroups are XCD-major (dispatch puts workgroup b on XCD b % 8):
 // the column groups of one (head group, sequence) are consecutive and run
 // together on one XCD, whose L2 then serves their re-reads of the same K/V.
-#ifndef PA_PF_WAVES
-#define PA_PF_WAVES 8           // waves (16-column tiles) per workgroup
-#endif
-#ifndef PA_PF_STAGES
-#define PA_PF_STAGES 2          // slots (tile pairs) in rotation, head_dim 128
-#endif
-constexpr int PF_WAVES = PA_PF_WAVES;
+//
+// Waves per workgroup: 16 at head_dim 128 (one workgroup per compute unit,
+// four waves per SIMD: every staged tile serves 256 columns; measured on
+// MI355X in one run, the prefix-cache call 998 against 1087 us per call with
+// 8, the 7B-shaped 512-row prefill unchanged), 8 at head_dim 256, whose worker
+// needs more registers than four waves per SIMD leave.  The shared-prefix
+// pass keeps 8 (its 128 sequences fill 8 column tiles; 16 measured 64.7
+// against 64.2 us per call).
+template <int D> struct PrefillWaves { static constexpr int value = D <= 128 ? 16 : 8; };
+constexpr int PREFIX_WAVES = 8;
+constexpr int PF_STAGES = 2;    // slots (tile pairs) in rotation
 
-template <typename T, int D, int BS, bool STREAM_KV>
+template <typename T, int D, int BS, bool STREAM_KV, int NW>
 struct PrefillTiles {
     using W = GqaWorker<T, D, BS, STREAM_KV>;
     static constexpr int NC = W::NC;                    // K chunks (and loads) per tile
@@ -69,9 +73,9 @@ struct PrefillTiles {
     static constexpr int BYTES = 2 * TILE_BYTES;        // one slot: a pair of tiles
     static constexpr int TILE_LOADS = NC + NL;
     static constexpr int LOADS = 2 * TILE_LOADS;
-    static constexpr int PER_WAVE = LOADS / PF_WAVES;
-    static constexpr int STAGES = D <= 128 ? PA_PF_STAGES : 2;
-    static_assert(LOADS % PF_WAVES == 0, "the loads of a slot share out evenly");
+    static constexpr int PER_WAVE = LOADS / NW;
+    static constexpr int STAGES = PF_STAGES;
+    static_assert(LOADS % NW == 0, "the loads of a slot share out evenly");
     // bf16 keeps P as hi + lo (8 significant bits would not meet the accuracy bound); f16 rounds it once
     static constexpr bool HILO = std::is_same<T, bf16_t>::value;
 };
@@ -79,11 +83,11 @@ struct PrefillTiles {
 // Key tiles t_begin .. t_end - 1 of the worker's kv head, staged in pairs
 // through LDS for all the waves of the workgroup (every wave calls this with
 // the same range); the wave computes the pairs that start below my_end.
-template <typename T, int D, int BS, bool STREAM_KV>
+template <typename T, int D, int BS, bool STREAM_KV, int NW>
 __device__ __forceinline__ void staged_tiles(GqaWorker<T, D, BS, STREAM_KV> &w, unsigned char PA_LDS *base, int wave,
                                              int lane, int t_begin, int t_end, int my_end)
 {
-    using PT = PrefillTiles<T, D, BS, STREAM_KV>;
+    using PT = PrefillTiles<T, D, BS, STREAM_KV, NW>;
     using W = typename PT::W;
     constexpr int STAGES = PT::STAGES;
     // K source rows of this lane (K loads: row i / 4, swizzled piece)
@@ -161,10 +165,12 @@ __device__ __forceinline__ void staged_tiles(GqaWorker<T, D, BS, STREAM_KV> &w, 
 }
 
 template <typename T, int D, int BS, bool STREAM_KV>
-__global__ __launch_bounds__(PF_WAVES * 64) void prefill_kernel(const DecodeParams P, int col_groups, int total_wg)
+__global__ __launch_bounds__(PrefillWaves<D>::value * 64) void prefill_kernel(const DecodeParams P, int col_groups,
+                                                                             int total_wg)
 {
     static_assert(D % 128 == 0, "the matrix-core worker needs head_dim 128 or 256");
-    using PT = PrefillTiles<T, D, BS, STREAM_KV>;
+    constexpr int NW = PrefillWaves<D>::value;
+    using PT = PrefillTiles<T, D, BS, STREAM_KV, NW>;
     using W = typename PT::W;
     constexpr int STAGES = PT::STAGES;
     __shared__ __attribute__((aligned(16))) unsigned char lds[STAGES * PT::BYTES];
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(PF_WAVES * 64) void prefill_kernel(const DecodePara
     nq = nq > P.total_q - q_first ? P.total_q - q_first : nq;
     const int gh = P.group / P.group_split;
     const int rows = GQA_TILE / gh;                       // query rows per column tile
-    const int i0g = cg * PF_WAVES * rows;
+    const int i0g = cg * NW * rows;
     if (i0g >= nq)
         return;
 
@@ -201,13 +207,13 @@ __global__ __launch_bounds__(PF_WAVES * 64) void prefill_kernel(const DecodePara
     w.init_lane(lane);
     w.bind_rows(P, s, hg, ctx, q_first, nq, active ? i0 : i0g);
     // key tiles of the group: up to the last position any of its rows attends
-    const int last_row = min(i0g + PF_WAVES * rows, nq) - 1;
+    const int last_row = min(i0g + NW * rows, nq) - 1;
     const int t_end = min(ctx, max(0, ctx - nq + last_row + 1));
     const int n_tiles = (t_end + GQA_TILE - 1) / GQA_TILE;
     const int my_tiles = active ? (w.t_last + GQA_TILE - 1) / GQA_TILE : 0;
 
     w.reset();
-    staged_tiles<T, D, BS, STREAM_KV>(w, (unsigned char PA_LDS *)lds, wave, lane, 0, n_tiles, my_tiles);
+    staged_tiles<T, D, BS, STREAM_KV, NW>(w, (unsigned char PA_LDS *)lds, wave, lane, 0, n_tiles, my_tiles);
     if (active)
         w.finish_rows(P, q_first, i0, nq);
 }
@@ -216,16 +222,16 @@ template <typename T, int D, int BS>
 hipError_t launch_prefill_shape(const DecodeParams &p, int max_query_len, hipStream_t st)
 {
     const int rows = GQA_TILE / (p.group / p.group_split);
+    constexpr int NW = PrefillWaves<D>::value;
     const int col_tiles = (max_query_len + rows - 1) / rows;
-    const int col_groups = (col_tiles + PF_WAVES - 1) / PF_WAVES;
+    const int col_groups = (col_tiles + NW - 1) / NW;
     const long long total = (long long)col_groups * p.num_kv_heads * p.group_split * p.num_seqs;
     if (total > (1LL << 30))
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)((total + 7) / 8 * 8));
     // every column group of a (head group, sequence) reads the same key tiles:
     // K and V are loaded with the caches' normal policy, whatever the flags say
-    hipLaunchKernelGGL((prefill_kernel<T, D, BS, false>), grid, dim3(PF_WAVES * 64), 0, st, p, col_groups,
-                       (int)total);
+    hipLaunchKernelGGL((prefill_kernel<T, D, BS, false>), grid, dim3(NW * 64), 0, st, p, col_groups, (int)total);
     return hipGetLastError();
 }
 
@@ -238,7 +244,7 @@ hipError_t launch_prefill_shape(const DecodeParams &p, int max_query_len, hipStr
 // prefill's rows but with no causal order -- each sequence sees the prefix
 // tokens below its own context.  The prefix is cut into chunks of `chunk`
 // tokens (a multiple of two tiles, chosen per call by the host), one
-// workgroup per (group of PF_WAVES column tiles, chunk, head group); each
+// workgroup per (group of PREFIX_WAVES column tiles, chunk, head group); each
 // (sequence, q head) leaves the chunk's (max, sum, unnormalised output) as
 // split-K partition `chunk`.  The decode kernels then take the sequences' own
 // blocks as the partitions after these, and the split-K reduce merges them
@@ -249,16 +255,16 @@ inline int prefix_workgroups_per_chunk(int num_seqs, int group, int group_split,
 {
     const int rows = GQA_TILE / (group / group_split);
     const int col_tiles = (num_seqs + rows - 1) / rows;
-    const int col_groups = (col_tiles + PF_WAVES - 1) / PF_WAVES;
+    const int col_groups = (col_tiles + PREFIX_WAVES - 1) / PREFIX_WAVES;
     return col_groups * num_kv_heads * group_split;
 }
 
 template <typename T, int D, int BS>
-__global__ __launch_bounds__(PF_WAVES * 64) void prefix_kernel(const DecodeParams P, int col_groups, int n_chunks,
+__global__ __launch_bounds__(PREFIX_WAVES * 64) void prefix_kernel(const DecodeParams P, int col_groups, int n_chunks,
                                                                int prefix_tokens, int chunk, int total_wg)
 {
     static_assert(D % 128 == 0, "the matrix-core worker needs head_dim 128 or 256");
-    using PT = PrefillTiles<T, D, BS, false>;
+    using PT = PrefillTiles<T, D, BS, false, PREFIX_WAVES>;
     using W = typename PT::W;
     __shared__ __attribute__((aligned(16))) unsigned char lds[PT::STAGES * PT::BYTES];
 
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(PF_WAVES * 64) void prefix_kernel(const DecodeParam
     const int hg = lg_id / col_groups / n_chunks;
     const int gh = P.group / P.group_split;
     const int rows = GQA_TILE / gh;
-    const int i0g = cg * PF_WAVES * rows;                // first sequence of the group (inside the batch)
+    const int i0g = cg * PREFIX_WAVES * rows;            // first sequence of the group (inside the batch)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i0 = i0g + wave * rows;
@@ -284,8 +290,8 @@ __global__ __launch_bounds__(PF_WAVES * 64) void prefix_kernel(const DecodeParam
     w.bind_prefix(P, hg, active ? i0 : i0g, c0, c1);
     w.reset();
     const int t_end = (c1 + GQA_TILE - 1) / GQA_TILE;
-    staged_tiles<T, D, BS, false>(w, (unsigned char PA_LDS *)lds, wave, lane, c0 / GQA_TILE, t_end,
-                                  active ? t_end : 0);
+    staged_tiles<T, D, BS, false, PREFIX_WAVES>(w, (unsigned char PA_LDS *)lds, wave, lane, c0 / GQA_TILE, t_end,
+                                                active ? t_end : 0);
     if (active)
         w.finish_partials(P, i0, c);
 }
@@ -297,7 +303,7 @@ hipError_t launch_prefix_shape(const DecodeParams &p, int prefix_tokens, int chu
         return hipErrorInvalidValue;
     const int rows = GQA_TILE / (p.group / p.group_split);
     const int col_tiles = (p.num_seqs + rows - 1) / rows;
-    const int col_groups = (col_tiles + PF_WAVES - 1) / PF_WAVES;
+    const int col_groups = (col_tiles + PREFIX_WAVES - 1) / PREFIX_WAVES;
     const int n_chunks = (prefix_tokens + chunk - 1) / chunk;
     if (n_chunks != p.first_partition)
         return hipErrorInvalidValue;
@@ -305,7 +311,7 @@ hipError_t launch_prefix_shape(const DecodeParams &p, int prefix_tokens, int chu
     if (total > (1LL << 30))
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)((total + 7) / 8 * 8));
-    hipLaunchKernelGGL((prefix_kernel<T, D, BS>), grid, dim3(PF_WAVES * 64), 0, st, p, col_groups, n_chunks,
+    hipLaunchKernelGGL((prefix_kernel<T, D, BS>), grid, dim3(PREFIX_WAVES * 64), 0, st, p, col_groups, n_chunks,
                        prefix_tokens, chunk, (int)total);
     return hipGetLastError();
 }
