@@ -22,6 +22,7 @@
 
 #include "pa_decode_gqa.h"
 #include "pa_device.h"
+#include "pa_prefill_wide.h"
 
 namespace pa {
 
@@ -334,6 +335,14 @@ hipError_t launch_prefix_dtype(const DecodeParams &p, int head_dim, int bs, int 
 template <typename T, int D>
 hipError_t launch_prefill_bs(const DecodeParams &p, int bs, int max_query_len, hipStream_t st)
 {
+    if constexpr (D == 128) {
+        switch (bs) {
+        case 8: return launch_prefill_wide<T, 8>(p, max_query_len, st);
+        case 16: return launch_prefill_wide<T, 16>(p, max_query_len, st);
+        case 32: return launch_prefill_wide<T, 32>(p, max_query_len, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (bs) {
     case 8: return launch_prefill_shape<T, D, 8>(p, max_query_len, st);
     case 16: return launch_prefill_shape<T, D, 16>(p, max_query_len, st);

@@ -1,0 +1,445 @@
+// pa_prefill_wide.h -- multi-token paged attention at head_dim 128 on the
+// 32x32x16 matrix-core products of gfx950 (v_mfma_f32_32x32x16_{f16,bf16}).
+//
+// Method: "vLLM 与 PagedAttention" (inference.mavenzero.com/case-studies/vllm),
+// section 二: K/V sit in fixed-size blocks reached through the sequence's
+// block table and are read block by block, the per-block results merged by an
+// online softmax; section 六 ("关键的工程优化"): a long prompt is prefilled in
+// chunks.  Query row i of a chunk of n rows over a context of L tokens sits at
+// position L - n + i and attends tokens 0 .. L - n + i (causal).
+//
+// A prefill reads each key for many query rows, so the work is a dense
+// product per (sequence, kv head) and wants the widest matrix tiles the
+// registers allow.  One wave owns 32 score columns -- 32 / gh query rows
+// times the gh q heads of one kv head -- and takes the keys 64 at a time:
+//
+//   S^T[32 keys x 32 cols] = K . Q^T     two per step, 8 products each (d = 128)
+//       A operand K from LDS (lane l: key l % 32, dims 16c + 8(l / 32) .. +8),
+//       B operand Q held in registers for the whole kernel.  Lane l then holds
+//       column l % 32 at keys 8(v / 4) + 4(l / 32) + v % 4 of the tile, v < 16.
+//   softmax   per column: the lane and its partner l ^ 32 hold all 64 keys; the
+//       reference max changes only when a step's max exceeds it by 2^8, so
+//       the accumulators are rarely rescaled.
+//   O^T[32 dims x 32 cols] += V^T . P^T  four dim tiles x four 16-key chunks
+//       B operand P^T straight from the lane's own probabilities (the eight of
+//       chunk c are registers 8(c % 2) .. +8 of tile c / 2: keys 16c +
+//       {4h .. 4h + 3, 8 + 4h .. 8 + 4h + 3} for h = l / 32), A operand V^T
+//       read from LDS with two transposed reads (ds_read_b64_tr_b16) whose
+//       keys follow that same order.
+//
+// The four waves of a workgroup (128 columns) share each step's K and V
+// tiles, staged in LDS by direct-to-LDS loads (no registers), two steps in
+// rotation.  A tile is 64 rows of 256 bytes, written in 1 KiB pieces of four
+// rows; inside a piece, 16-byte unit u of row k sits at slot
+// 16 (k % 4) + (u ^ s(k)) with s(k) = 4 (k % 4) + (k / 4) % 4.  Each
+// 16-lane group of a load then reads one whole 256-byte row (coalesced), the
+// K operand reads (16 rows, one unit) and the transposed V reads (4 rows x 4
+// units per 32 lanes) fall on distinct LDS banks.
+//
+// Rows past the context or in a block outside the pool are staged as zeros
+// (their loads read a zero buffer), and partial steps (the causal diagonal,
+// the context's end, such blocks) mask the scores to -inf: whatever that
+// memory holds -- NaN included -- never reaches the accumulators.  f16 rounds P once and the
+// running sum adds the rounded values (v_dot2_f32_f16); bf16 keeps P as
+// hi + lo in two products.
+#pragma once
+
+#include <type_traits>
+
+#include "pa_decode_gqa.h"
+#include "pa_device.h"
+
+namespace pa {
+
+typedef float wide_f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename T> struct WideOps;
+template <> struct WideOps<f16_t> {
+    __device__ __forceinline__ static wide_f32x16 mma(const uint4 &a, const uint4 &b, wide_f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(gqa_f16x8, a),
+                                                      __builtin_bit_cast(gqa_f16x8, b), c, 0, 0, 0);
+    }
+};
+template <> struct WideOps<bf16_t> {
+    __device__ __forceinline__ static wide_f32x16 mma(const uint4 &a, const uint4 &b, wide_f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(gqa_bf16x8, a),
+                                                       __builtin_bit_cast(gqa_bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+constexpr int WIDE_WAVES = 4;                        // waves per workgroup
+constexpr int WIDE_COLS = 32;                        // score columns per wave
+constexpr int WIDE_STEP = 64;                        // keys per step
+constexpr int WIDE_TILE = WIDE_STEP * 256;           // bytes of K (or V) per step at head_dim 128
+constexpr int WIDE_STAGE = 2 * WIDE_TILE;            // K then V
+constexpr int WIDE_STAGES = 2;
+constexpr float WIDE_RESCALE_LOG2 = 8.f;
+
+// the source of every direct-load lane whose row lies past the context or in a
+// block outside the pool
+static __device__ __attribute__((aligned(16))) const uint4 wide_zero = {0u, 0u, 0u, 0u};
+
+template <typename T, int BS>
+__global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_wide_kernel(
+    const DecodeParams P, int col_groups, int total_wg)
+{
+    constexpr int D = 128;
+    constexpr int ES = 2;
+    constexpr bool HILO = std::is_same<T, bf16_t>::value;
+    constexpr int NE = WIDE_STEP / BS;                 // table entries per step
+    static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[WIDE_STAGES * WIDE_STAGE];
+    unsigned char PA_LDS *const lds = (unsigned char PA_LDS *)lds_raw;
+
+    // logical workgroups XCD-major (dispatch puts workgroup b on XCD b % 8):
+    // the column groups of one (head group, sequence) run together on one XCD
+    const int per_xcd = (total_wg + 7) / 8;
+    const int lg_id = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (lg_id >= total_wg)
+        return;
+    const int HG = P.num_kv_heads * P.group_split;
+    const int cg = lg_id % col_groups;
+    const int hg = (lg_id / col_groups) % HG;
+    const int s = lg_id / col_groups / HG;
+
+    int ctx = P.ctx[s];
+    const int cap = P.max_blocks * BS;
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    const int q_first = P.query_start[s];
+    int nq = P.query_start[s + 1] - q_first;
+    if (q_first < 0 || q_first >= P.total_q)
+        return;
+    nq = nq > P.total_q - q_first ? P.total_q - q_first : nq;
+    const int gh = P.group / P.group_split;
+    const int R = WIDE_COLS / gh;                       // query rows per wave
+    const int ncols = R * gh;
+    const int i0g = cg * WIDE_WAVES * R;
+    if (i0g >= nq)
+        return;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i0 = i0g + wave * R;
+    const bool wave_on = i0 < nq;
+    const int j = lane & 31;                            // score column
+    const int h = lane >> 5;                            // key half of the column's scores
+    const int row = i0 + j / gh;
+    const bool on = wave_on && j < ncols && row < nq;
+    auto limit = [&](int r) { const int t = ctx - nq + r + 1; return t < 0 ? 0 : (t > ctx ? ctx : t); };
+    const int t_full = limit(i0);                       // every column of the wave sees keys below this
+    const int t_hi = on ? limit(row) : t_full;          // this column's keys: [0, t_hi)
+    const int wave_end = wave_on ? limit(min(i0 + R, nq) - 1) : 0;
+    const int wg_end = limit(min(i0g + WIDE_WAVES * R, nq) - 1);
+    const int n_steps = (wg_end + WIDE_STEP - 1) / WIDE_STEP;
+
+    const int kvh = hg / P.group_split;
+    const int qh0 = kvh * P.group + (hg - kvh * P.group_split) * gh;
+    const int64_t blk_bytes = P.block_stride * ES;
+    const int64_t tok_bytes = P.token_stride * ES;
+    const char *kpool = static_cast<const char *>(P.k) + (int64_t)kvh * P.head_stride * ES;
+    const char *vpool = static_cast<const char *>(P.v) + (int64_t)kvh * P.head_stride * ES;
+    const int32_t __attribute__((address_space(4))) *trow =
+        (const int32_t __attribute__((address_space(4))) *)(P.tables + (int64_t)s * P.max_blocks);
+    const int nblk = (ctx + BS - 1) / BS;
+    const int num_blocks = P.num_blocks;
+    const float sl2 = P.scale_log2;
+
+    // Q^T operand of column j: dims 16c + 8h .. +8 for c < 8.  Every lane
+    // loads (an idle column reads the sequence's first row) and the select
+    // waits for the loads here: none is still counted as in flight inside
+    // the loop, whose own vector-memory waits must cover the tile loads only
+    uint4 qb[8];
+    {
+        const char *qp = static_cast<const char *>(P.q) +
+                         (((int64_t)(q_first + (on ? row : 0)) * P.num_q_heads + qh0 + (on ? j % gh : 0)) * D + 8 * h) *
+                             ES;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint4 v = ld16(qp + 32 * c);
+            qb[c] = on ? v : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+
+    // direct loads: lane p brings row p / 16 of the piece, unit (p % 16) ^ s(row)
+    const uint32_t ld_row = (uint32_t)((lane >> 4) * tok_bytes);
+    const uint32_t ld_unit = (uint32_t)((16 * (lane & 15)) ^ (64 * (lane >> 4)));
+    // K operand: key l % 32 of the tile, unit 2c + h
+    const int kl = lane & 31;
+    const uint32_t k_base = 1024 * (kl >> 2) + 256 * (kl & 3);
+    const uint32_t k_x = (uint32_t)(h ^ (4 * (kl & 3) + ((kl >> 2) & 3)));
+    // V operand, transposed reads: source lane (group g, index i) addresses key
+    // 16c + 8rho + 4h + i / 4, dims 32dt + 16(g % 2) + 4(i % 4) .. +4
+    const int vi = lane & 15;
+    const int vgd = (lane >> 4) & 1;
+    const uint32_t v_a = 1024 * h + 256 * (vi >> 2) + 16 * ((2 * vgd + ((vi & 3) >> 1)) ^ h) + 8 * (vi & 1);
+    const uint32_t v_b = 64 * (vi >> 2);
+
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    // the table entries of a step (clamped to the sequence's last block; a
+    // block past it holds only rows past the context).  Each step's entries
+    // are fetched two steps ahead, so the scalar loads are never waited for.
+    auto fetch = [&](int step, int (&ent)[NE]) {
+        const int b = step * (WIDE_STEP / BS);
+        if (b + NE <= nblk) {
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                ent[e] = trow[b + e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                ent[e] = trow[min(b + e, nblk - 1)];
+        }
+    };
+
+    // step `step` into stage `st`: waves 0-1 bring K, 2-3 bring V, eight
+    // 1 KiB pieces each (rows 32 (wave % 2) + 4jj .. +4 of the step).  A row
+    // past the context or in a block outside the pool is read from 16 zero
+    // bytes instead: its K scores are masked, and its V row, all zero, adds
+    // nothing (the products never see what such memory holds)
+    auto issue = [&](int step, int st, const int (&ent)[NE]) {
+        const int tok = step * WIDE_STEP + 32 * (wave & 1);
+        const char *pool = (wave >> 1) ? vpool : kpool;
+        const uint32_t dst = lds0 + st * WIDE_STAGE + (wave >> 1) * WIDE_TILE + 8192 * (wave & 1);
+        constexpr int PER_BLK = BS / 4 < 8 ? BS / 4 : 8;   // pieces per block entry
+        constexpr int HALF = NE / 2;                       // first entry of rows 32 ..
+#pragma unroll
+        for (int e = 0; e < 8 / PER_BLK; ++e) {
+            const int lo_e = ent[e], hi_e = ent[HALF + e];      // constant indices: the array stays in registers
+            const int raw = (wave & 1) ? hi_e : lo_e;
+            const bool mapped = (unsigned)raw < (unsigned)num_blocks;
+            const char *blk = pool + (uint64_t)(uint32_t)(mapped ? raw : 0) * (uint64_t)blk_bytes;
+            const int t_e = tok + 4 * PER_BLK * e;             // first row of the entry's pieces
+            if (mapped && t_e + 4 * PER_BLK <= ctx) {
+#pragma unroll
+                for (int jj = e * PER_BLK; jj < (e + 1) * PER_BLK; ++jj)
+                    load_lds_sbase<false>(blk + (int64_t)((4 * jj) % BS) * tok_bytes,
+                                          ld_row + (ld_unit ^ (16u * (jj & 3))), dst + 1024 * jj);
+            } else {
+#pragma unroll
+                for (int jj = e * PER_BLK; jj < (e + 1) * PER_BLK; ++jj) {
+                    const bool ok = mapped && tok + 4 * jj + (lane >> 4) < ctx;
+                    const char *src = blk + (int64_t)((4 * jj) % BS) * tok_bytes + ld_row + (ld_unit ^ (16u * (jj & 3)));
+                    load_lds_asm<false>(ok ? src : reinterpret_cast<const char *>(&wide_zero), dst + 1024 * jj);
+                }
+            }
+        }
+    };
+
+    wide_f32x16 acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            acc[dt][v] = 0.f;
+    float m = NEG_BIG;                                  // reference max of column j (log2 units)
+    float lp = 0.f;                                     // this lane's share of the column's sum
+
+    // the products and the softmax of one step
+    auto compute = [&](int t0, uint32_t okm, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        const unsigned char PA_LDS *stg = lds + ST * WIDE_STAGE;
+        // (a negative scale also takes the masked path: the other one takes the
+        // max of the raw scores)
+        const bool masked =
+            t0 + WIDE_STEP > t_full || t0 + WIDE_STEP > ctx || okm != (1u << NE) - 1u || !(sl2 >= 0.f);
+
+        // all sixteen K fragments of the step are requested before the first
+        // product: the reads' latency is paid once per step, not per product
+        gqa_u32x4 kf[2][8];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                kf[kt][c] = *reinterpret_cast<const gqa_u32x4 PA_LDS *>(stg + 8192 * kt + k_base + 16 * (k_x ^ (2 * c)));
+        __builtin_amdgcn_sched_barrier(0);
+        wide_f32x16 sc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                sc[kt][v] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                sc[kt] = WideOps<T>::mma(make_uint4(kf[kt][c].x, kf[kt][c].y, kf[kt][c].z, kf[kt][c].w), qb[c], sc[kt]);
+
+        // the step's max of column j in log2 units, and the factor that takes
+        // a raw score there (masked steps scale and mask first)
+        float mx, f;
+        if (masked) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int kr = 32 * kt + 8 * (v >> 2);             // first key of the 8-key group
+                    const int key = t0 + kr + 4 * h + (v & 3);
+                    const bool ok = ((okm >> (kr / BS)) & 1u) && key < t_hi;
+                    sc[kt][v] = ok ? sc[kt][v] * sl2 : -INFINITY;
+                }
+            mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    mx = fmaxf(mx, sc[kt][v]);
+            f = 1.f;
+        } else {
+            float hi = sc[0][0];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    hi = fmaxf(hi, sc[kt][v]);
+            mx = hi * sl2;
+            f = sl2;
+        }
+        {
+            const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        }
+        const bool grow = mx > m + WIDE_RESCALE_LOG2;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float mn = grow ? mx : m;
+            const float alpha = fast_exp2(m - mn);
+            m = mn;
+            lp *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[dt][v] *= alpha;
+        }
+
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int kt = c >> 1, v0 = 8 * (c & 1);
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                p[e] = fast_exp2(__builtin_fmaf(sc[kt][v0 + e], f, -m));
+            uint4 phi, plo = make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (HILO) {
+                phi = make_uint4(GqaOps<T>::pack(p[0], p[1]), GqaOps<T>::pack(p[2], p[3]),
+                                 GqaOps<T>::pack(p[4], p[5]), GqaOps<T>::pack(p[6], p[7]));
+                float w[8];
+                GqaOps<T>::unpack(phi.x, w[0], w[1]);
+                GqaOps<T>::unpack(phi.y, w[2], w[3]);
+                GqaOps<T>::unpack(phi.z, w[4], w[5]);
+                GqaOps<T>::unpack(phi.w, w[6], w[7]);
+                plo = make_uint4(GqaOps<T>::pack(p[0] - w[0], p[1] - w[1]), GqaOps<T>::pack(p[2] - w[2], p[3] - w[3]),
+                                 GqaOps<T>::pack(p[4] - w[4], p[5] - w[5]), GqaOps<T>::pack(p[6] - w[6], p[7] - w[7]));
+                lp += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            } else {
+                phi = make_uint4(GqaOps<T>::pack(p[0], p[1]), GqaOps<T>::pack(p[2], p[3]),
+                                 GqaOps<T>::pack(p[4], p[5]), GqaOps<T>::pack(p[6], p[7]));
+                const half2v one = {(_Float16)1.f, (_Float16)1.f};
+                lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, phi.x), one, lp, false);
+                lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, phi.y), one, lp, false);
+                lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, phi.z), one, lp, false);
+                lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, phi.w), one, lp, false);
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const unsigned char PA_LDS *vs = stg + WIDE_TILE + 4096 * c;
+                const uint2 r0 = GqaOps<T>::read_tr(vs + (v_a + ((64u * dt) ^ v_b)));
+                const uint2 r1 = GqaOps<T>::read_tr(vs + 2048 + ((v_a ^ 32u) + ((64u * dt) ^ v_b)));
+                const uint4 va = make_uint4(r0.x, r0.y, r1.x, r1.y);
+                acc[dt] = WideOps<T>::mma(va, phi, acc[dt]);
+                if constexpr (HILO)
+                    acc[dt] = WideOps<T>::mma(va, plo, acc[dt]);
+            }
+        }
+    };
+
+    // one step out of stage ST (a constant, so that every LDS read takes its
+    // stage as an immediate offset: the loop below runs the steps in pairs)
+    // one step out of stage ST (a constant, so that every LDS read takes its
+    // stage as an immediate offset: the loop below runs the steps in pairs).
+    // ent_a holds the entries of this step, ent_b those of the next; the
+    // entries two steps ahead are fetched after the products, so that their
+    // scalar loads stay in flight across the barrier (which waits for vector
+    // loads only: every LDS read of the stage the next loads fill has been
+    // consumed by then)
+    int ent_a[NE], ent_b[NE];
+    auto run_step = [&](int step, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        // this wave's loads of the step have landed; at the barrier every
+        // wave's have, and every wave is done with the stage the next loads fill
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (step + 1 < n_steps)
+            issue(step + 1, ST ^ 1, ent_b);
+        // blocks of the step that lie in the pool (bit e: keys e BS .. +BS)
+        uint32_t okm = 0;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            okm |= ((unsigned)ent_a[e] < (unsigned)num_blocks ? 1u : 0u) << e;
+            ent_a[e] = ent_b[e];
+        }
+        const int t0 = step * WIDE_STEP;
+        if (t0 < wave_end)
+            compute(t0, okm, st_c);
+        if (step + 2 < n_steps)
+            fetch(step + 2, ent_b);
+    };
+
+    if (n_steps > 0) {
+        fetch(0, ent_a);
+        if (n_steps > 1)
+            fetch(1, ent_b);
+        issue(0, 0, ent_a);
+    }
+    for (int step = 0; step < n_steps; step += 2) {
+        run_step(step, std::integral_constant<int, 0>());
+        if (step + 1 < n_steps)
+            run_step(step + 1, std::integral_constant<int, 1>());
+    }
+
+    // every load into LDS has landed before the workgroup ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!wave_on)
+        return;
+    {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(lp), false, false);
+        lp = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    if (!on)
+        return;
+    const float inv = lp > 0.f ? 1.f / lp : 0.f;
+    char *op = static_cast<char *>(P.out) +
+               (((int64_t)(q_first + row) * P.num_q_heads + qh0 + j % gh) * D + 4 * h) * ES;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                o[r] = acc[dt][4 * g + r] * inv;
+            uint2 w;
+            if constexpr (HILO) {
+                w.x = (uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
+                w.y = (uint32_t)f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16);
+            } else {
+                w.x = (uint32_t)f32_to_f16_bits(o[0]) | ((uint32_t)f32_to_f16_bits(o[1]) << 16);
+                w.y = (uint32_t)f32_to_f16_bits(o[2]) | ((uint32_t)f32_to_f16_bits(o[3]) << 16);
+            }
+            *reinterpret_cast<uint2 *>(op + (32 * dt + 8 * g) * ES) = w;
+        }
+}
+
+template <typename T, int BS>
+hipError_t launch_prefill_wide(const DecodeParams &p, int max_query_len, hipStream_t st)
+{
+    const int rows = WIDE_COLS / (p.group / p.group_split);
+    const int per_wg = WIDE_WAVES * rows;
+    const int col_groups = (max_query_len + per_wg - 1) / per_wg;
+    const long long total = (long long)col_groups * p.num_kv_heads * p.group_split * p.num_seqs;
+    if (total > (1LL << 30))
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((total + 7) / 8 * 8));
+    hipLaunchKernelGGL((prefill_wide_kernel<T, BS>), grid, dim3(WIDE_WAVES * 64), 0, st, p, col_groups, (int)total);
+    return hipGetLastError();
+}
+
+}  // namespace pa
