@@ -112,9 +112,7 @@ template <> struct GqaOps<f16_t> {
     }
 };
 
-#ifndef PA_GQA_STAGES
-#define PA_GQA_STAGES 3         // tiles in flight per wave (registers for K, LDS for V)
-#endif
+constexpr int GQA_STAGES = 3;          // tiles in flight per wave (registers for K, LDS for V)
 constexpr int GQA_TILE = 16;    // tokens per tile
 constexpr float GQA_RESCALE_LOG2 = 8.f;   // rescale when a head's max grows by more than 2^8
 
@@ -255,7 +253,7 @@ struct GqaWorker {
     static constexpr int LOAD_LDS = 1024 + 128; // bytes of LDS per direct load (with padding)
     static constexpr int TILE_LDS = NL * LOAD_LDS;
     // head_dim 256 holds twice the K registers per tile: two tiles in rotation
-    static constexpr int STAGES = D <= 128 ? PA_GQA_STAGES : 2;
+    static constexpr int STAGES = D <= 128 ? GQA_STAGES : 2;
     static constexpr int LDS_BYTES = STAGES * TILE_LDS;
     static constexpr int STEP_TOK = GQA_TILE;   // tokens per step of the schedule
     static constexpr int LOADS_PER_TILE = NC + NL;   // vector-memory operations load() issues

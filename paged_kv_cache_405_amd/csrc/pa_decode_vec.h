@@ -35,15 +35,9 @@
 
 namespace pa {
 
-#ifndef PA_VEC_STAGES
-#define PA_VEC_STAGES 2         // steps in the register pipeline of the vector kernel
-#endif
-#ifndef PA_VEC_NLD
-#define PA_VEC_NLD 2            // most wave-wide loads of K (and of V) per step
-#endif
-#ifndef PA_VEC_WAVES_PER_EU
-#define PA_VEC_WAVES_PER_EU 1   // occupancy floor handed to the register allocator
-#endif
+constexpr int VEC_STAGES = 2;          // steps in the register pipeline of the vector kernel
+constexpr int VEC_NLD = 2;             // most wave-wide loads of K (and of V) per step
+constexpr int VEC_WAVES_PER_EU = 1;    // occupancy floor handed to the register allocator (1 = none)
 
 // One wave's share of the work on one (sequence, kv head): the online-softmax
 // state of GT query heads and the step pipeline that feeds it.  A step is a
@@ -63,7 +57,7 @@ struct VecWorker {
     static constexpr int ROWS = TPL < BS ? TPL : BS; // rows that carry tokens
     static constexpr bool ALL_ROWS = TPL <= BS;
     static constexpr int NLD_TILE = BS / ROWS;       // wave-wide loads per (block, kv head) tile
-    static constexpr int NLD = NLD_TILE < PA_VEC_NLD ? NLD_TILE : PA_VEC_NLD;   // loads per step (a slab of the tile)
+    static constexpr int NLD = NLD_TILE < VEC_NLD ? NLD_TILE : VEC_NLD;   // loads per step (a slab of the tile)
     static constexpr int NSLAB = NLD_TILE / NLD;     // steps per tile
     static constexpr int SLAB_TOK = NLD * ROWS;      // tokens per step
 
@@ -268,7 +262,7 @@ struct VecWorker {
 
     // steps qbeg, qbeg + stride, ... below qend (wave-uniform)
     __device__ __forceinline__ void run(int qbeg, int qend, int stride) {
-        pipeline<PA_VEC_STAGES>(*this, qbeg, qend, stride);
+        pipeline<VEC_STAGES>(*this, qbeg, qend, stride);
     }
 
     // merge the token rows of the wave (lanes that differ in the row bits)
@@ -293,7 +287,7 @@ struct VecWorker {
 };
 
 template <typename T, int D, int BS, int GT, int NW, bool STREAM_KV>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_VEC_WAVES_PER_EU)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(VEC_WAVES_PER_EU)))
 void decode_vec_kernel(const DecodeParams P)
 {
     using W = VecWorker<T, D, BS, GT, STREAM_KV>;
@@ -432,10 +426,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(const DecodeParams P)
 // ---------------------------------------------------------------------------
 // host-side dispatch over the compile-time shape
 // ---------------------------------------------------------------------------
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 4
-#endif
-constexpr int DECODE_WAVES = PA_DECODE_WAVES;
+constexpr int DECODE_WAVES = 4;
 
 template <typename T, int D, int BS, int GT>
 hipError_t launch_decode_shape(const DecodeParams &p, hipStream_t st)

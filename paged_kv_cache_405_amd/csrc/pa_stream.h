@@ -70,16 +70,10 @@ __device__ __forceinline__ uint64_t range_start(int w, uint64_t T, int N) {
     return q * (uint64_t)w + (r * (uint64_t)w) / (uint64_t)N;
 }
 
-#ifndef PA_STREAM_XCD_MAJOR
-#define PA_STREAM_XCD_MAJOR 1      // 1: logical waves assigned XCD major
-#endif
-
-#ifndef PA_STREAM_WAVES_PER_EU
-#define PA_STREAM_WAVES_PER_EU 1   // waves per SIMD the register allocation must allow (1 = no limit)
-#endif
+constexpr int STREAM_WAVES_PER_EU = 1;   // waves per SIMD the register allocation must allow (1 = no limit)
 
 template <class W, int BS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_STREAM_WAVES_PER_EU)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(STREAM_WAVES_PER_EU)))
 void decode_stream_kernel(const DecodeParams P)
 {
     constexpr int STEP = W::STEP_TOK;
@@ -111,7 +105,7 @@ void decode_stream_kernel(const DecodeParams P)
     }
     const uint64_t T = (uint64_t)tseq * (uint64_t)HG;
     const int bid = blockIdx.x;
-    const int w = PA_STREAM_XCD_MAJOR ? (bid & 7) * (N >> 3) + (bid >> 3) : bid;
+    const int w = (bid & 7) * (N >> 3) + (bid >> 3);   // logical waves XCD-major
     if (bid == 0 && lane == 0)
         P.stream_total[0] = T;
     const uint64_t c_lo = range_start(w, T, N);
