@@ -182,7 +182,7 @@ def prefix_cache_step(args):
         "speedup": round(ms["full"] / ms["cached"], 2),
         "prompt_tokens_from_cache": round(sum(hits[i] for i in later) / prompt_tokens, 4),
         "host_us_per_request": round(host_us, 3),
-        "roofline": {"kernel": "prefill_kernel (the cached call)", "bound": "mfma", "achieved": round(achieved, 2),
+        "roofline": {"kernel": "prefill_wide_kernel (the cached call)", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": None, "avg_call_us": round(ms["cached"] * 1e3, 3), "flops_per_call": flops},
         "cpu_baseline": {"value": round(1e6 / model_us, 1), "unit": "requests admitted/s", "cores": 1,
@@ -262,7 +262,7 @@ def prefill_step(args):
         "vs_baseline": None, "dtype": "f16", "data": "synthetic (normal draws)",
         "config": {"workload": f"prefill: {S} seqs x {chunk}-token chunk over {hist} cached tokens, {H}x{D} MHA, "
                                f"fp16, bs {bs}, {layers} layers", "chunk": chunk, "history": hist},
-        "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+        "roofline": {"kernel": "prefill_wide_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": None, "avg_call_us": round(call_ms * 1e3, 3), "flops_per_call": flops},
         "cpu_baseline": {"value": round(flops / S / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
