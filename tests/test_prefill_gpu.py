@@ -2,8 +2,10 @@
 oracle (oracle/prefill.py): from-scratch prefills, chunks over a cached
 history, single rows (decode), chunks longer than their context, every block
 size, both head dims and group shapes from MHA to 32 q heads per kv head;
-the append-then-attend flow of a chunked prefill; and the rows that
-query_start leaves outside q are never touched."""
+the append-then-attend flow of a chunked prefill; the rows that
+query_start leaves outside q are never touched; a block outside the pool
+(adds nothing), a negative scale, the pages' cache layout, and grouped heads
+spread over many workgroups of one (head group, sequence)."""
 import numpy as np
 import pytest
 import torch
@@ -128,3 +130,84 @@ def test_chunked_prefill_append_then_attend(dtype, Hq, Hkv):
         torch.cuda.synchronize()
         ref = paged_prefill(q_all[pos], kc, vc, table, ctx, np.array([0, n], np.int32), scale, dtype)
         assert_close(compare(out, ref, dtype), dtype, f"chunk ending at {done}")
+
+
+@pytest.mark.parametrize("dtype,D,bs,Hq,Hkv", [("f16", 128, 16, 8, 8), ("bf16", 128, 8, 16, 4),
+                                               ("f16", 128, 32, 32, 1), ("bf16", 256, 16, 8, 8)])
+def test_unmapped_block_contributes_nothing(dtype, D, bs, Hq, Hkv):
+    """A table entry outside [0, num_blocks) is never read and adds nothing:
+    with one whole block of a history unmapped, every row attends the other
+    tokens, which is the same as the history with that block taken out (the
+    rows all sit after it, so their causal limits move with them)."""
+    ctxs, counts = [300, 90, 200], [40, 30, 1]
+    w = W.custom(f"prefill_unmapped_{dtype}_{D}_{bs}_{Hq}x{Hkv}", dtype, ctxs, Hq, Hkv, D, bs, seed=5 + bs,
+                 append=False, table_pad=1)
+    rng = np.random.default_rng(6 + bs)
+    q_np = W.to_storage(rng.standard_normal((sum(counts), Hq, D), dtype=np.float32), dtype)
+    hole = [2, 0, 64 // bs]                               # a block below every row of the sequence
+    tables = w.block_tables.copy()
+    for s, b in enumerate(hole):
+        assert (b + 1) * bs <= ctxs[s] - counts[s]
+        tables[s, b] = w.num_blocks + 123 if s != 1 else -7
+    g = upload(w)
+    qs = _starts(counts)
+    q = to_dev(q_np, dtype)
+    out = torch.full_like(q, float("nan"))
+    B.pa_prefill(out, q, g.k_cache, g.v_cache, torch.from_numpy(tables).cuda(), g.ctx, torch.from_numpy(qs).cuda(),
+                 max(counts), w.scale, num_blocks=w.num_blocks)
+    torch.cuda.synchronize()
+    # the oracle over the tables with the hole removed and each context one block shorter
+    packed = np.full_like(w.block_tables, -1)
+    for s, b in enumerate(hole):
+        row = [e for i, e in enumerate(w.block_tables[s]) if i != b]
+        packed[s, :len(row)] = row
+    ctx2 = np.array([c - bs for c in ctxs], np.int32)
+    ref = paged_prefill(q_np, w.k_cache, w.v_cache, packed, ctx2, qs, w.scale, dtype)
+    log(f"[gpu] prefill {w.name}")
+    assert_close(compare(out, ref, dtype), dtype, f"{w.name}: one block unmapped")
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 128), ("bf16", 128), ("f16", 256)])
+def test_negative_scale(dtype, D):
+    """The scale's sign flips which score is the largest; the kernels take the
+    max after scaling (the oracle's definition, any finite scale)."""
+    ctxs, counts = [150, 64], [150, 20]
+    scale = -1.0 / np.sqrt(D)
+    w = W.custom(f"prefill_negscale_{dtype}_{D}", dtype, ctxs, 16, 4, D, 16, seed=12, append=False, scale=scale)
+    rng = np.random.default_rng(13)
+    q_np = W.to_storage(rng.standard_normal((sum(counts), 16, D), dtype=np.float32), dtype)
+    g = upload(w)
+    log(f"[gpu] prefill {w.name}")
+    out, ref = _run(w, g, q_np, counts)
+    assert_close(compare(out, ref, dtype), dtype, w.name)
+
+
+@pytest.mark.parametrize("dtype,bs", [("f16", 16), ("bf16", 8)])
+def test_pages_layout_agrees(dtype, bs):
+    """The pages' cache layout [NB, bs, Hkv, D] (token rows Hkv x D apart)
+    against the oracle, and bit for bit against the default layout."""
+    ctxs, counts = [260, 33, 129], [100, 33, 9]
+    w = W.custom(f"prefill_bthd_{dtype}_{bs}", dtype, ctxs, 32, 8, 128, bs, seed=21 + bs, append=False)
+    rng = np.random.default_rng(22 + bs)
+    q_np = W.to_storage(rng.standard_normal((sum(counts), 32, 128), dtype=np.float32), dtype)
+    g_bthd = upload(w, B.PA_LAYOUT_BTHD)
+    log(f"[gpu] prefill {w.name}")
+    out, ref = _run(w, g_bthd, q_np, counts)
+    assert_close(compare(out, ref, dtype), dtype, f"{w.name} (pages' layout)")
+    out_bhtd, _ = _run(w, upload(w), q_np, counts)
+    assert torch.equal(out, out_bhtd)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(64, 8), (48, 3), (64, 4)])
+def test_grouped_heads_over_many_column_groups(Hq, Hkv):
+    """Groups of 8, 16 and 16 q heads (64 / 4 splits into head groups of 16)
+    take 4 or 2 query rows per wave, so 200 rows span many workgroups of one
+    (head group, sequence), each with its own causal limits."""
+    ctxs, counts = [420, 200], [200, 57]
+    w = W.custom(f"prefill_groups_{Hq}x{Hkv}", "f16", ctxs, Hq, Hkv, 128, 16, seed=Hq + Hkv, append=False)
+    rng = np.random.default_rng(Hq * Hkv)
+    q_np = W.to_storage(rng.standard_normal((sum(counts), Hq, 128), dtype=np.float32), "f16")
+    g = upload(w)
+    log(f"[gpu] prefill {w.name}")
+    out, ref = _run(w, g, q_np, counts)
+    assert_close(compare(out, ref, "f16"), "f16", w.name)
