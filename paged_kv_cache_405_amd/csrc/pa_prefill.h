@@ -53,14 +53,12 @@ namespace pa {
 // the column groups of one (head group, sequence) are consecutive and run
 // together on one XCD, whose L2 then serves their re-reads of the same K/V.
 //
-// Waves per workgroup: 16 at head_dim 128 (one workgroup per compute unit,
-// four waves per SIMD: every staged tile serves 256 columns; measured on
-// MI355X in one run, the prefix-cache call 998 against 1087 us per call with
-// 8, the 7B-shaped 512-row prefill unchanged), 8 at head_dim 256, whose worker
-// needs more registers than four waves per SIMD leave.  The shared-prefix
-// pass keeps 8 (its 128 sequences fill 8 column tiles; 16 measured 64.7
-// against 64.2 us per call).
-template <int D> struct PrefillWaves { static constexpr int value = D <= 128 ? 16 : 8; };
+// pa_prefill takes this kernel at head_dim 256 (head_dim 128 has the 32x32x16
+// kernel of pa_prefill_wide.h), with 8 waves per workgroup: the worker needs
+// more registers than four waves per SIMD leave.  The shared-prefix pass
+// below runs 8-wave workgroups at both head dims (its 128 sequences fill 8
+// column tiles; 16 waves measured 64.7 against 64.2 us per call).
+constexpr int PREFILL_WAVES = 8;
 constexpr int PREFIX_WAVES = 8;
 constexpr int PF_STAGES = 2;    // slots (tile pairs) in rotation
 
@@ -166,11 +164,11 @@ __device__ __forceinline__ void staged_tiles(GqaWorker<T, D, BS, STREAM_KV> &w, 
 }
 
 template <typename T, int D, int BS, bool STREAM_KV>
-__global__ __launch_bounds__(PrefillWaves<D>::value * 64) void prefill_kernel(const DecodeParams P, int col_groups,
+__global__ __launch_bounds__(PREFILL_WAVES * 64) void prefill_kernel(const DecodeParams P, int col_groups,
                                                                              int total_wg)
 {
     static_assert(D % 128 == 0, "the matrix-core worker needs head_dim 128 or 256");
-    constexpr int NW = PrefillWaves<D>::value;
+    constexpr int NW = PREFILL_WAVES;
     using PT = PrefillTiles<T, D, BS, STREAM_KV, NW>;
     using W = typename PT::W;
     constexpr int STAGES = PT::STAGES;
@@ -223,7 +221,7 @@ template <typename T, int D, int BS>
 hipError_t launch_prefill_shape(const DecodeParams &p, int max_query_len, hipStream_t st)
 {
     const int rows = GQA_TILE / (p.group / p.group_split);
-    constexpr int NW = PrefillWaves<D>::value;
+    constexpr int NW = PREFILL_WAVES;
     const int col_tiles = (max_query_len + rows - 1) / rows;
     const int col_groups = (col_tiles + NW - 1) / NW;
     const long long total = (long long)col_groups * p.num_kv_heads * p.group_split * p.num_seqs;
@@ -342,12 +340,13 @@ hipError_t launch_prefill_bs(const DecodeParams &p, int bs, int max_query_len, h
         case 32: return launch_prefill_wide<T, 32>(p, max_query_len, st);
         default: return hipErrorInvalidValue;
         }
-    }
-    switch (bs) {
-    case 8: return launch_prefill_shape<T, D, 8>(p, max_query_len, st);
-    case 16: return launch_prefill_shape<T, D, 16>(p, max_query_len, st);
-    case 32: return launch_prefill_shape<T, D, 32>(p, max_query_len, st);
-    default: return hipErrorInvalidValue;
+    } else {
+        switch (bs) {
+        case 8: return launch_prefill_shape<T, D, 8>(p, max_query_len, st);
+        case 16: return launch_prefill_shape<T, D, 16>(p, max_query_len, st);
+        case 32: return launch_prefill_shape<T, D, 32>(p, max_query_len, st);
+        default: return hipErrorInvalidValue;
+        }
     }
 }
 
