@@ -601,17 +601,33 @@ pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
         return PA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < pp.ws_bytes || !aligned(workspace, 16))
         return PA_ERR_WORKSPACE;
+    // Both passes go in one launch when the own blocks take the vector kernel
+    // (pa_shared_prefix.h): the prefix pass's workgroups then run beside the
+    // own-blocks pass instead of before it.
+    const bool combined = prefix_blocks > 0 && pp.max_partitions > pp.n_chunks && !pp.suffix.mfma &&
+                          (pp.suffix.gt == 1 || pp.suffix.gt == 2);
     // every argument checked (the workspace against the smallest chunk's plan,
-    // as the query states it): the device's compute units choose the chunk
+    // as the query states it): the chunk of the call.  Beside the own-blocks
+    // pass, few long chunks: fewer prefix workgroups taking room from it and
+    // fewer partials for the reduce (measured on the shared-prefix workload:
+    // 64.2 us per call as two launches, 62.8 / 61.1 / 57.9 / 54.7 / 54.5 /
+    // 59.9 / 69.3 us combined with chunks of 192 / 256 / 384 / 512 / 768 /
+    // 1024 / 1504 tokens).  Alone, about one workgroup per compute unit.
     if (prefix_blocks > 0) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            return PA_ERR_HIP;
-        const int group = num_q_heads / num_kv_heads;
-        const int chunk = prefix_chunk(prefix_blocks * block_size,
-                                       pa::prefix_workgroups(num_seqs, group, pp.prefix_group_split, num_kv_heads),
-                                       cus);
+        const int prefix_tokens = prefix_blocks * block_size;
+        int chunk;
+        if (combined) {
+            chunk = std::min(pa::SHARED_PREFIX_CHUNK_MAX,
+                             std::max(pa::SHARED_PREFIX_CHUNK_MIN, (prefix_tokens + 31) / 32 * 32));
+        } else {
+            int dev = 0, cus = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+                return PA_ERR_HIP;
+            const int group = num_q_heads / num_kv_heads;
+            chunk = prefix_chunk(prefix_tokens,
+                                 pa::prefix_workgroups(num_seqs, group, pp.prefix_group_split, num_kv_heads), cus);
+        }
         st = make_prefix_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
                               prefix_blocks, chunk, &pp);
         if (st != PA_OK)
@@ -643,6 +659,19 @@ pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
     p.partition_blocks = PA_SUFFIX_TOKENS(block_size) / block_size;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
+    // both passes in one launch (their data is disjoint; the reduce follows both)
+    if (combined) {
+        pa::DecodeParams px = p, sx = p;
+        px.group_split = pp.prefix_group_split;
+        sx.group_split = pp.suffix.group_split;
+        e = dtype == PA_F16 ? pa::launch_shared_prefix_f16(sx, px, head_dim, block_size, pp.suffix.gt,
+                                                          prefix_blocks * block_size, pp.chunk, s)
+                            : pa::launch_shared_prefix_bf16(sx, px, head_dim, block_size, pp.suffix.gt,
+                                                           prefix_blocks * block_size, pp.chunk, s);
+        if (e != hipSuccess)
+            return PA_ERR_HIP;
+        return pa::launch_reduce(p, (int)dtype, head_dim, block_size, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
+    }
     // the prefix, once for the whole batch
     if (pp.n_chunks > 0) {
         pa::DecodeParams px = p;

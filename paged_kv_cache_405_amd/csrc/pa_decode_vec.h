@@ -286,17 +286,19 @@ struct VecWorker {
     }
 };
 
+// The grid kernels' workgroup (partition bx of head group by of grid row bz),
+// as a function of its block coordinates: the shared-prefix decode runs it
+// inside a launch of its own (pa_shared_prefix.h).
 template <typename T, int D, int BS, int GT, int NW, bool STREAM_KV>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(VEC_WAVES_PER_EU)))
-void decode_vec_kernel(const DecodeParams P)
+__device__ __forceinline__ void decode_vec_block(const DecodeParams &P, int bx, int by, int bz)
 {
     using W = VecWorker<T, D, BS, GT, STREAM_KV>;
     constexpr int VEC = W::VEC;
 
-    const int p = blockIdx.x + P.first_partition;
-    const int hg = blockIdx.y;
+    const int p = bx + P.first_partition;
+    const int hg = by;
     int ctx;
-    const int s = seq_of_row(P, blockIdx.z, BS, ctx);
+    const int s = seq_of_row(P, bz, BS, ctx);
     const int nblk = (ctx + BS - 1) / BS;
     const int npart = num_partitions(P, nblk);
     if (p >= npart)
@@ -377,6 +379,13 @@ void decode_vec_kernel(const DecodeParams P)
             emit(g, d, M, L, A);
         }
     }
+}
+
+template <typename T, int D, int BS, int GT, int NW, bool STREAM_KV>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(VEC_WAVES_PER_EU)))
+void decode_vec_kernel(const DecodeParams P)
+{
+    decode_vec_block<T, D, BS, GT, NW, STREAM_KV>(P, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Split-K reduce: one wave per (q head, sequence) merges the partitions'

@@ -258,26 +258,24 @@ inline int prefix_workgroups_per_chunk(int num_seqs, int group, int group_split,
     return col_groups * num_kv_heads * group_split;
 }
 
-template <typename T, int D, int BS>
-__global__ __launch_bounds__(PREFIX_WAVES * 64) void prefix_kernel(const DecodeParams P, int col_groups, int n_chunks,
-                                                               int prefix_tokens, int chunk, int total_wg)
+// One workgroup of the prefix pass (NW waves; logical workgroup lg_id of
+// total_wg): also run inside the shared-prefix decode's combined launch
+// (pa_shared_prefix.h), next to the workgroups of the own-blocks pass.
+template <typename T, int D, int BS, int NW>
+__device__ __forceinline__ void prefix_block(const DecodeParams &P, int lg_id, int col_groups, int n_chunks,
+                                             int prefix_tokens, int chunk)
 {
     static_assert(D % 128 == 0, "the matrix-core worker needs head_dim 128 or 256");
-    using PT = PrefillTiles<T, D, BS, false, PREFIX_WAVES>;
+    using PT = PrefillTiles<T, D, BS, false, NW>;
     using W = typename PT::W;
     __shared__ __attribute__((aligned(16))) unsigned char lds[PT::STAGES * PT::BYTES];
 
-    // XCD-major, column groups fastest: the groups reading one chunk of one kv head share an L2
-    const int per_xcd = (total_wg + 7) / 8;
-    const int lg_id = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if (lg_id >= total_wg)
-        return;
     const int cg = lg_id % col_groups;
     const int c = (lg_id / col_groups) % n_chunks;
     const int hg = lg_id / col_groups / n_chunks;
     const int gh = P.group / P.group_split;
     const int rows = GQA_TILE / gh;
-    const int i0g = cg * PREFIX_WAVES * rows;            // first sequence of the group (inside the batch)
+    const int i0g = cg * NW * rows;                      // first sequence of the group (inside the batch)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i0 = i0g + wave * rows;
@@ -289,10 +287,22 @@ __global__ __launch_bounds__(PREFIX_WAVES * 64) void prefix_kernel(const DecodeP
     w.bind_prefix(P, hg, active ? i0 : i0g, c0, c1);
     w.reset();
     const int t_end = (c1 + GQA_TILE - 1) / GQA_TILE;
-    staged_tiles<T, D, BS, false, PREFIX_WAVES>(w, (unsigned char PA_LDS *)lds, wave, lane, c0 / GQA_TILE, t_end,
-                                                active ? t_end : 0);
+    staged_tiles<T, D, BS, false, NW>(w, (unsigned char PA_LDS *)lds, wave, lane, c0 / GQA_TILE, t_end,
+                                      active ? t_end : 0);
     if (active)
         w.finish_partials(P, i0, c);
+}
+
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(PREFIX_WAVES * 64) void prefix_kernel(const DecodeParams P, int col_groups, int n_chunks,
+                                                               int prefix_tokens, int chunk, int total_wg)
+{
+    // XCD-major, column groups fastest: the groups reading one chunk of one kv head share an L2
+    const int per_xcd = (total_wg + 7) / 8;
+    const int lg_id = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (lg_id >= total_wg)
+        return;
+    prefix_block<T, D, BS, PREFIX_WAVES>(P, lg_id, col_groups, n_chunks, prefix_tokens, chunk);
 }
 
 template <typename T, int D, int BS>
