@@ -389,12 +389,35 @@ void decode_vec_kernel(const DecodeParams P)
 }
 
 // Split-K reduce: one wave per (q head, sequence) merges the partitions'
-// (max, sum, unnormalised output) and writes the normalised output.
+// (max, sum, unnormalised output) and writes the normalised output.  Every
+// (q head, sequence) has max_partitions slots, so the slots of the first
+// REDUCE_FEW partitions are loaded at once, beside the context length that
+// says how many of them are real: one memory round trip instead of three.
+// Slots past the real partitions hold whatever an earlier call left there;
+// they are selected out, never multiplied by a zero weight.  Partitions are
+// added in order whatever the path, so results are bit-reproducible.
+constexpr int REDUCE_FEW = 8;
+
 template <typename T, int D, int BS>
 __global__ __launch_bounds__(64) void reduce_kernel(const DecodeParams P)
 {
+    constexpr int E = (D + 63) / 64;
     const int qh = blockIdx.x;
     const int s = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int64_t sh = (int64_t)s * P.num_q_heads + qh;
+    const float2 *ml = P.ws_ml + sh * P.max_partitions;
+    const float *acc = P.ws_acc + sh * P.max_partitions * D;
+    const int nfew = min(REDUCE_FEW, P.max_partitions);
+    const int nlane = min(64, P.max_partitions);
+    const float2 mlv = lane < nlane ? ml[lane] : make_float2(NEG_BIG, 0.f);
+    float a[REDUCE_FEW][E];
+#pragma unroll
+    for (int i = 0; i < REDUCE_FEW; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            a[i][e] = i < nfew && lane + 64 * e < D ? acc[(int64_t)i * D + lane + 64 * e] : 0.f;
+
     int ctx = P.ctx[s];
     const int cap = P.max_blocks * BS;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
@@ -402,34 +425,45 @@ __global__ __launch_bounds__(64) void reduce_kernel(const DecodeParams P)
     const int npart = num_partitions(P, nblk);
     if (npart <= 1 && P.first_partition == 0)
         return;
-    const int lane = threadIdx.x;
-    const int64_t sh = (int64_t)s * P.num_q_heads + qh;
-    const float2 *ml = P.ws_ml + sh * P.max_partitions;
-    const float *acc = P.ws_acc + sh * P.max_partitions * D;
 
-    float M = NEG_BIG;
-    for (int i = lane; i < npart; i += 64)
-        M = fmaxf(M, ml[i].x);
-    M = group_max<64>(M);
-    float L = 0.f;
-    for (int i = lane; i < npart; i += 64) {
+    // lane i < 64 holds partition i; partitions past 64 in a loop
+    float mx = lane < npart ? mlv.x : NEG_BIG;
+    for (int i = lane + 64; i < npart; i += 64)
+        mx = fmaxf(mx, ml[i].x);
+    const float M = group_max<64>(mx);
+    const float c = lane < npart ? fast_exp2(mlv.x - M) : 0.f;
+    float L = lane < npart ? mlv.y * c : 0.f;
+    for (int i = lane + 64; i < npart; i += 64) {
         const float2 v = ml[i];
         L = fmaf(v.y, fast_exp2(v.x - M), L);
     }
     L = group_sum<64>(L);
-    // the partitions' loads do not depend on one another: unrolled, several
-    // are in flight at once
+
+    float A[E];
 #pragma unroll
-    for (int d0 = 0; d0 < D; d0 += 64) {
-        const int d = d0 + lane;
-        if (d < D) {
-            float A = 0.f;
-#pragma unroll 4
-            for (int i = 0; i < npart; ++i)
-                A = fmaf(acc[(int64_t)i * D + d], fast_exp2(ml[i].x - M), A);
-            Store<T>::one(P.out, sh * D + d, L > 0.f ? A / L : 0.f);
+    for (int e = 0; e < E; ++e)
+        A[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < REDUCE_FEW; ++i) {
+        if (i < npart) {
+            const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), i));
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                A[e] = fmaf(a[i][e], ci, A[e]);
         }
     }
+    for (int i = REDUCE_FEW; i < npart; ++i) {
+        const float ci = i < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), i))
+                                : fast_exp2(ml[i].x - M);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (lane + 64 * e < D)
+                A[e] = fmaf(acc[(int64_t)i * D + lane + 64 * e], ci, A[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (lane + 64 * e < D)
+            Store<T>::one(P.out, sh * D + lane + 64 * e, L > 0.f ? A[e] / L : 0.f);
 }
 
 // ---------------------------------------------------------------------------
