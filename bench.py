@@ -542,7 +542,10 @@ def decode_run(args, w, cfg, layers, steps, warmup, torch, B, repeats=REPEATS, w
         path_name, call_kernels = f"split-K {path_pt} tokens", f"decode_{family}_kernel + reduce_kernel"
     if prefix_pass:
         path_name = f"shared prefix ({w.shared_prefix_blocks} blocks) once, then split-K"
-        call_kernels = f"prefix_kernel + decode_{family}_kernel (the sequences' own blocks) + reduce_kernel"
+        # the library runs both passes in one launch when the own blocks take the vector kernel
+        call_kernels = ("shared_prefix_kernel (the prefix pass beside the sequences' own blocks) + reduce_kernel"
+                        if family == "vec" else
+                        f"prefix_kernel + decode_{family}_kernel (the sequences' own blocks) + reduce_kernel")
     log(f"[bench] {w.name}: path {path_name}, kernels per call: {call_kernels}")
 
     def decode(out, q, kc, vc):
