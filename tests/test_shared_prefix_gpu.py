@@ -4,7 +4,9 @@ shared-prefix workload (128 sequences, 94 shared blocks), and edge cases --
 prefixes of 1 to 20 blocks (one to three prefix chunks, the last one
 partial), contexts shorter than, equal to and longer than
 the prefix, an empty context, every block size, both head dims and dtypes,
-grouped-query ratios up to 32 -- and the plain decode path agrees too."""
+grouped-query ratios 1, 2, 3, 8 and 32 (both launch forms: the prefix pass
+beside a vector own-blocks pass in one launch, or before a matrix-core one)
+-- and the plain decode path agrees too."""
 import numpy as np
 import pytest
 import torch
@@ -43,6 +45,10 @@ def _cases():
                     if D == 256 and Hq == 64:
                         continue
                     out.append((dtype, D, bs, Hq, Hkv))
+            # small groups keep the own blocks on the vector kernel, in the one-launch form: two q heads per
+            # workgroup (16 over 8), and three heads split one per workgroup (12 over 4)
+            for Hq, Hkv in ((16, 8), (12, 4)):
+                out.append((dtype, D, 16, Hq, Hkv))
     return out
 
 
