@@ -281,6 +281,47 @@ pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *
                      pa_layout layout, unsigned flags, void *stream);
 
 /*
+ * pa_prefill_shared_prefix -- pa_prefill for a batch whose block tables all
+ * start with the same prefix_blocks physical blocks: requests admitted with
+ * automatic prefix caching, which point at the cached blocks of a shared
+ * prompt ("vLLM 与 PagedAttention" section 四, the shared system prompt;
+ * "指南", "Copy-on-Write：Prefix Caching 的基础").  The same function: row i of
+ * sequence s attends tokens 0 .. L - n + i of its own history.  The prefix's
+ * K/V are read once for the whole batch -- the rows of every sequence are the
+ * columns of one matrix-core pass over them, each capped at its own causal
+ * limit -- and each sequence then reads its keys past the prefix and merges.
+ *
+ *   prefix_blocks   0 .. max_blocks_per_seq: row 0 of block_tables lists the
+ *                   prefix's blocks in its first prefix_blocks entries (those
+ *                   are the ones read, whatever context_lens[0] is); in every
+ *                   other row, the entries that are both inside the prefix and
+ *                   below the row's own block count must be the same blocks
+ *   workspace       device memory, 16-byte aligned, at least
+ *                   pa_prefill_shared_prefix_workspace_bytes(total_q,
+ *                   num_q_heads, head_dim, block_size, prefix_blocks) bytes
+ *                   (content on entry does not matter): the prefix's partial
+ *                   result of every (row, q head), (8 + 4 head_dim) bytes
+ *                   each; may be null when that size is 0
+ *   other arguments as for pa_prefill (no flags)
+ *
+ * The keys read once for every row are the whole 64-token steps inside the
+ * prefix; the rest of the prefix is read per sequence with its own keys.  With
+ * a prefix shorter than 64 tokens, or at head_dim 256, it computes exactly as
+ * pa_prefill (no workspace).  Errors as for pa_prefill; PA_ERR_INVALID_ARG for
+ * prefix_blocks out of range; PA_ERR_WORKSPACE for a missing, short or
+ * misaligned workspace.
+ */
+pa_status pa_prefill_shared_prefix(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *block_tables, const int32_t *context_lens,
+                                   const int32_t *query_start, int num_seqs, int total_q, int max_query_len,
+                                   int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                   int max_blocks_per_seq, int num_blocks, int prefix_blocks, float scale,
+                                   pa_dtype dtype, pa_layout layout, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+pa_status pa_prefill_shared_prefix_workspace_bytes(int total_q, int num_q_heads, int head_dim, int block_size,
+                                                   int prefix_blocks, size_t *bytes_out);
+
+/*
  * pa_decode_shared_prefix -- pa_decode_ex for a batch whose block tables all
  * start with the same prefix_blocks physical blocks (a shared system prompt;
  * requests that point at the same blocks, "vLLM 与 PagedAttention" section

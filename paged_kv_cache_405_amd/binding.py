@@ -119,6 +119,10 @@ def lib():
             L.pa_bm_info.argtypes = [vp, i64, pi64, pi32, pi32]
             L.pa_prefill.restype = i32
             L.pa_prefill.argtypes = [vp] * 7 + [i32] * 9 + [f32, i32, i32, ctypes.c_uint32, vp]
+            L.pa_prefill_shared_prefix.restype = i32
+            L.pa_prefill_shared_prefix.argtypes = [vp] * 7 + [i32] * 10 + [f32, i32, i32, vp, sz, vp]
+            L.pa_prefill_shared_prefix_workspace_bytes.restype = i32
+            L.pa_prefill_shared_prefix_workspace_bytes.argtypes = [i32] * 5 + [ctypes.POINTER(sz)]
             L.pa_status_string.restype = ctypes.c_char_p
             L.pa_probe_stream_read.restype = i32
             L.pa_probe_stream_read.argtypes = [vp, sz, vp, i32, i32, vp]
@@ -322,6 +326,42 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start
         PA_DECODE_SHARED_BLOCKS if shared_blocks else 0, _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_prefill")
+    return out
+
+
+def pa_prefill_shared_prefix_workspace_bytes(total_q, num_q_heads, head_dim, block_size, prefix_blocks):
+    out = ctypes.c_size_t(0)
+    st = lib().pa_prefill_shared_prefix_workspace_bytes(total_q, num_q_heads, head_dim, block_size, prefix_blocks,
+                                                        ctypes.byref(out))
+    if st != PA_OK:
+        raise PaError(st, "pa_prefill_shared_prefix_workspace_bytes")
+    return out.value
+
+
+def pa_prefill_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len,
+                             scale, prefix_blocks, *, num_blocks=None, layout=PA_LAYOUT_BHTD, workspace=None,
+                             stream=None):
+    """pa_prefill for tables that all start with the same prefix_blocks blocks (their K/V read once for every
+    sequence's rows)."""
+    torch = _torch()
+    code = _dtype_code(q)
+    TQ, Hq, D = q.shape
+    NB, bs, Hkv, D2 = cache_dims(k_cache, layout)
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, out and the caches")
+    S = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(query_start.shape) != (S + 1,):
+        raise ValueError("block_tables must be [S, MB], context_lens [S] and query_start [S + 1]")
+    nbytes = pa_prefill_shared_prefix_workspace_bytes(TQ, Hq, D, bs, int(prefix_blocks))
+    ws, ws_bytes = _workspace(q, nbytes, workspace)
+    st = lib().pa_prefill_shared_prefix(
+        _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        _dev(query_start, "query_start", torch.int32), S, TQ, int(max_query_len), Hq, Hkv, D, bs,
+        block_tables.shape[1], NB if num_blocks is None else int(num_blocks), int(prefix_blocks), float(scale), code,
+        int(layout), None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_prefill_shared_prefix")
     return out
 
 

@@ -720,12 +720,16 @@ pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void
                               block_size, num_blocks, dtype, layout, static_cast<hipStream_t>(stream));
 }
 
-pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
-                     const int32_t *block_tables, const int32_t *context_lens, const int32_t *query_start,
-                     int num_seqs, int total_q, int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
-                     int block_size, int max_blocks_per_seq, int num_blocks, float scale, pa_dtype dtype,
-                     pa_layout layout, unsigned flags, void *stream)
+namespace {
+
+// the checks and launch parameters of the prefill entry points; *done: nothing to compute
+pa_status prefill_setup(void *out, const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_tables, const int32_t *context_lens, const int32_t *query_start,
+                        int num_seqs, int total_q, int max_query_len, int num_q_heads, int num_kv_heads,
+                        int head_dim, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                        pa_dtype dtype, pa_layout layout, unsigned flags, pa::DecodeParams *p, bool *done)
 {
+    *done = false;
     if (flags & ~(unsigned)PA_DECODE_SHARED_BLOCKS)
         return PA_ERR_INVALID_ARG;
     pa_status st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
@@ -739,39 +743,124 @@ pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *
         return PA_ERR_INVALID_ARG;
     if (num_seqs > 65535 || (long long)num_kv_heads * (group <= 16 ? 1 : group / 16) > 65535)
         return PA_ERR_UNSUPPORTED;
-    if (num_seqs == 0 || total_q == 0 || max_query_len == 0)
+    if (num_seqs == 0 || total_q == 0 || max_query_len == 0) {
+        *done = true;
         return PA_OK;
+    }
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
         return PA_ERR_INVALID_ARG;
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
         return PA_ERR_INVALID_ARG;
 
+    std::memset(p, 0, sizeof(*p));
+    p->out = out;
+    p->q = q;
+    p->k = k_cache;
+    p->v = v_cache;
+    p->tables = block_tables;
+    p->ctx = context_lens;
+    p->query_start = query_start;
+    p->total_q = total_q;
+    p->kv_cached = (flags & PA_DECODE_SHARED_BLOCKS) ? 1 : 0;
+    layout_strides(layout, num_kv_heads, block_size, head_dim, &p->block_stride, &p->head_stride, &p->token_stride);
+    p->num_seqs = num_seqs;
+    p->num_q_heads = num_q_heads;
+    p->num_kv_heads = num_kv_heads;
+    p->max_blocks = max_blocks_per_seq;
+    p->num_blocks = num_blocks;
+    p->partition_blocks = max_blocks_per_seq;
+    p->max_partitions = 1;
+    p->group = group;
+    p->group_split = group <= 16 ? 1 : group / 16;
+    p->scale_log2 = (float)((double)scale * 1.4426950408889634);
+    return PA_OK;
+}
+
+// the prefix partials of the shared-prefix prefill: (max, sum) then the
+// unnormalised output of every (q row, q head)
+size_t prefill_partial_ml_bytes(int total_q, int num_q_heads)
+{
+    return round_up((size_t)total_q * num_q_heads * sizeof(float2), WS_ALIGN);
+}
+
+}  // namespace
+
+pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, const int32_t *context_lens, const int32_t *query_start,
+                     int num_seqs, int total_q, int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int block_size, int max_blocks_per_seq, int num_blocks, float scale, pa_dtype dtype,
+                     pa_layout layout, unsigned flags, void *stream)
+{
     pa::DecodeParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.out = out;
-    p.q = q;
-    p.k = k_cache;
-    p.v = v_cache;
-    p.tables = block_tables;
-    p.ctx = context_lens;
-    p.query_start = query_start;
-    p.total_q = total_q;
-    p.kv_cached = (flags & PA_DECODE_SHARED_BLOCKS) ? 1 : 0;
-    layout_strides(layout, num_kv_heads, block_size, head_dim, &p.block_stride, &p.head_stride, &p.token_stride);
-    p.num_seqs = num_seqs;
-    p.num_q_heads = num_q_heads;
-    p.num_kv_heads = num_kv_heads;
-    p.max_blocks = max_blocks_per_seq;
-    p.num_blocks = num_blocks;
-    p.partition_blocks = max_blocks_per_seq;
-    p.max_partitions = 1;
-    p.group = group;
-    p.group_split = group <= 16 ? 1 : group / 16;
-    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    bool done = false;
+    const pa_status st = prefill_setup(out, q, k_cache, v_cache, block_tables, context_lens, query_start, num_seqs,
+                                       total_q, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, num_blocks, scale, dtype, layout, flags, &p, &done);
+    if (st != PA_OK || done)
+        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = dtype == PA_F16 ? pa::launch_prefill_f16(p, head_dim, block_size, max_query_len, s)
                                          : pa::launch_prefill_bf16(p, head_dim, block_size, max_query_len, s);
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_prefill_shared_prefix_workspace_bytes(int total_q, int num_q_heads, int head_dim, int block_size,
+                                                   int prefix_blocks, size_t *bytes_out)
+{
+    if (!bytes_out)
+        return PA_ERR_INVALID_ARG;
+    *bytes_out = 0;
+    if (total_q < 0 || num_q_heads <= 0 || prefix_blocks < 0)
+        return PA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (head_dim != 128 || pa::wide_prefix_split(prefix_blocks, block_size) == 0 || total_q == 0)
+        return PA_OK;   // computed as pa_prefill: no workspace
+    *bytes_out = prefill_partial_ml_bytes(total_q, num_q_heads) +
+                 (size_t)total_q * num_q_heads * head_dim * sizeof(float);
+    return PA_OK;
+}
+
+pa_status pa_prefill_shared_prefix(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *block_tables, const int32_t *context_lens,
+                                   const int32_t *query_start, int num_seqs, int total_q, int max_query_len,
+                                   int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                   int max_blocks_per_seq, int num_blocks, int prefix_blocks, float scale,
+                                   pa_dtype dtype, pa_layout layout, void *workspace, size_t workspace_bytes,
+                                   void *stream)
+{
+    pa::DecodeParams p;
+    bool done = false;
+    pa_status st = prefill_setup(out, q, k_cache, v_cache, block_tables, context_lens, query_start, num_seqs,
+                                 total_q, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 max_blocks_per_seq, num_blocks, scale, dtype, layout, 0u, &p, &done);
+    if (st != PA_OK)
+        return st;
+    if (prefix_blocks < 0 || prefix_blocks > max_blocks_per_seq)
+        return PA_ERR_INVALID_ARG;
+    if (done)
+        return PA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (head_dim != 128 || pa::wide_prefix_split(prefix_blocks, block_size) == 0) {
+        // less than one whole step to share, or the head_dim-256 kernel (no shared-prefix form): every row
+        // over its whole history
+        e = dtype == PA_F16 ? pa::launch_prefill_f16(p, head_dim, block_size, max_query_len, s)
+                            : pa::launch_prefill_bf16(p, head_dim, block_size, max_query_len, s);
+        return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+    }
+    size_t need = 0;
+    st = pa_prefill_shared_prefix_workspace_bytes(total_q, num_q_heads, head_dim, block_size, prefix_blocks, &need);
+    if (st != PA_OK)
+        return st;
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+        return PA_ERR_WORKSPACE;
+    p.part_base_blocks = prefix_blocks;
+    p.ws_ml = reinterpret_cast<float2 *>(workspace);
+    p.ws_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + prefill_partial_ml_bytes(total_q, num_q_heads));
+    e = dtype == PA_F16 ? pa::launch_prefill_shared_f16(p, block_size, max_query_len, s)
+                        : pa::launch_prefill_shared_bf16(p, block_size, max_query_len, s);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -140,6 +140,15 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
+// keys per step of the head_dim-128 prefill kernel, and the keys its
+// shared-prefix form reads once for every row: the whole steps inside a
+// prefix of `blocks` blocks of `bs` tokens (host and device)
+constexpr int PREFILL_WIDE_STEP = 64;
+__host__ __device__ constexpr int wide_prefix_split(int blocks, int bs)
+{
+    return blocks * bs / PREFILL_WIDE_STEP * PREFILL_WIDE_STEP;
+}
+
 constexpr int DPP_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int DPP_HMIRROR = 0x141; // row_half_mirror

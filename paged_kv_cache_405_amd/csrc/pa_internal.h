@@ -36,6 +36,11 @@ hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t st);
 // multi-token paged attention on the matrix cores (f16 / bf16, head_dim 128 or 256)
 hipError_t launch_prefill_f16(const DecodeParams &p, int head_dim, int block_size, int max_query_len, hipStream_t st);
 hipError_t launch_prefill_bf16(const DecodeParams &p, int head_dim, int block_size, int max_query_len, hipStream_t st);
+// the shared-prefix form of it at head_dim 128: the prefix's keys (p.part_base_blocks blocks of table row 0)
+// for the rows of every sequence at once, partials to p.ws_ml / p.ws_acc; then each sequence's own keys,
+// merged with those partials
+hipError_t launch_prefill_shared_f16(const DecodeParams &p, int block_size, int max_query_len, hipStream_t st);
+hipError_t launch_prefill_shared_bf16(const DecodeParams &p, int block_size, int max_query_len, hipStream_t st);
 // shared-prefix decode, first pass: the prefix's split-K partitions 0 .. first_partition - 1,
 // one per chunk of the prefix; a chunk is a multiple of 32 tokens in [SHARED_PREFIX_CHUNK_MIN,
 // SHARED_PREFIX_CHUNK_MAX], chosen per call

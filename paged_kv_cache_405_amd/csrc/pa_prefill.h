@@ -361,6 +361,17 @@ hipError_t launch_prefill_bs(const DecodeParams &p, int bs, int max_query_len, h
 }
 
 template <typename T>
+hipError_t launch_prefill_shared_bs(const DecodeParams &p, int bs, int max_query_len, hipStream_t st)
+{
+    switch (bs) {
+    case 8: return launch_prefill_shared_wide<T, 8>(p, max_query_len, st);
+    case 16: return launch_prefill_shared_wide<T, 16>(p, max_query_len, st);
+    case 32: return launch_prefill_shared_wide<T, 32>(p, max_query_len, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
 hipError_t launch_prefill_dtype(const DecodeParams &p, int head_dim, int bs, int max_query_len, hipStream_t st)
 {
     switch (head_dim) {

@@ -9,6 +9,11 @@ hipError_t launch_prefill_f16(const DecodeParams &p, int head_dim, int block_siz
     return launch_prefill_dtype<f16_t>(p, head_dim, block_size, max_query_len, st);
 }
 
+hipError_t launch_prefill_shared_f16(const DecodeParams &p, int block_size, int max_query_len, hipStream_t st)
+{
+    return launch_prefill_shared_bs<f16_t>(p, block_size, max_query_len, st);
+}
+
 hipError_t launch_prefix_f16(const DecodeParams &p, int head_dim, int block_size, int prefix_tokens, int chunk,
                              hipStream_t st)
 {

@@ -69,17 +69,60 @@ template <> struct WideOps<bf16_t> {
 
 constexpr int WIDE_WAVES = 4;                        // waves per workgroup
 constexpr int WIDE_COLS = 32;                        // score columns per wave
-constexpr int WIDE_STEP = 64;                        // keys per step
+constexpr int WIDE_STEP = PREFILL_WIDE_STEP;         // keys per step
 constexpr int WIDE_TILE = WIDE_STEP * 256;           // bytes of K (or V) per step at head_dim 128
 constexpr int WIDE_STAGE = 2 * WIDE_TILE;            // K then V
 constexpr int WIDE_STAGES = 2;
 constexpr float WIDE_RESCALE_LOG2 = 8.f;
 
+// what a launch computes (the shared-prefix form runs WIDE_PREFIX, then WIDE_OWN)
+constexpr int WIDE_PLAIN = 0;    // every row over its whole causal history
+constexpr int WIDE_PREFIX = 1;   // the shared prefix only, the rows of all sequences as columns: partials out
+constexpr int WIDE_OWN = 2;      // each sequence's keys past the prefix, merged with the prefix partials
+
+// the sequence whose rows hold q row r: the largest s < num_seqs with
+// query_start[s] <= r (r wave-uniform).  Each round narrows the range with 64
+// probes, one per lane (three rounds cover 65535 sequences); entries out of
+// order end the search early, never out of range.
+__device__ __forceinline__ int wide_seq_of_row(const DecodeParams &P, int r)
+{
+    const int lane = threadIdx.x & 63;
+    int lo = 0, hi = P.num_seqs;
+    while (hi - lo > 1) {
+        const int step = (hi - lo + 63) / 64;
+        const int k = lo + lane * step;
+        const uint64_t m = __ballot(k < hi && P.query_start[k] <= r);
+        if (m == 0)
+            break;
+        const int last = 63 - __builtin_clzll(m);
+        lo = __builtin_amdgcn_readfirstlane(lo + last * step);
+        hi = __builtin_amdgcn_readfirstlane(min(hi, lo + step));
+    }
+    return lo;
+}
+
+__device__ __forceinline__ int wide_wave_min(int x) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1)
+        x = min(x, __shfl_xor(x, off));
+    return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ int wide_wave_max(int x) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1)
+        x = max(x, __shfl_xor(x, off));
+    return __builtin_amdgcn_readfirstlane(x);
+}
+
 // the source of every direct-load lane whose row lies past the context or in a
 // block outside the pool
 static __device__ __attribute__((aligned(16))) const uint4 wide_zero = {0u, 0u, 0u, 0u};
 
-template <typename T, int BS>
+// MODE: WIDE_PLAIN, WIDE_PREFIX or WIDE_OWN (above).  The shared prefix holds
+// P.part_base_blocks blocks: in WIDE_PREFIX the keys are those blocks of table
+// row 0 and one virtual sequence holds all total_q rows, each column capped at
+// its own sequence's causal limit; in WIDE_OWN the keys start past the prefix.
+template <typename T, int BS, int MODE>
 __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_wide_kernel(
     const DecodeParams P, int col_groups, int total_wg)
 {
@@ -102,14 +145,25 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     const int hg = (lg_id / col_groups) % HG;
     const int s = lg_id / col_groups / HG;
 
-    int ctx = P.ctx[s];
     const int cap = P.max_blocks * BS;
-    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-    const int q_first = P.query_start[s];
-    int nq = P.query_start[s + 1] - q_first;
-    if (q_first < 0 || q_first >= P.total_q)
-        return;
-    nq = nq > P.total_q - q_first ? P.total_q - q_first : nq;
+    // the passes split the keys at the last whole step inside the shared prefix: the prefix pass takes the
+    // steps below it, unmasked by the prefix's end, and the own pass starts on a step boundary
+    const int prefix_tok = MODE == WIDE_PLAIN ? 0 : wide_prefix_split(P.part_base_blocks, BS);
+    // the keys this launch reads end at ctx; its rows are q[q_first .. q_first + nq)
+    int ctx, q_first, nq;
+    if constexpr (MODE == WIDE_PREFIX) {
+        ctx = prefix_tok;
+        q_first = 0;
+        nq = P.total_q;
+    } else {
+        ctx = P.ctx[s];
+        ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+        q_first = P.query_start[s];
+        nq = P.query_start[s + 1] - q_first;
+        if (q_first < 0 || q_first >= P.total_q)
+            return;
+        nq = nq > P.total_q - q_first ? P.total_q - q_first : nq;
+    }
     const int gh = P.group / P.group_split;
     const int R = WIDE_COLS / gh;                       // query rows per wave
     const int ncols = R * gh;
@@ -126,11 +180,44 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     const int row = i0 + j / gh;
     const bool on = wave_on && j < ncols && row < nq;
     auto limit = [&](int r) { const int t = ctx - nq + r + 1; return t < 0 ? 0 : (t > ctx ? ctx : t); };
-    const int t_full = limit(i0);                       // every column of the wave sees keys below this
-    const int t_hi = on ? limit(row) : t_full;          // this column's keys: [0, t_hi)
-    const int wave_end = wave_on ? limit(min(i0 + R, nq) - 1) : 0;
-    const int wg_end = limit(min(i0g + WIDE_WAVES * R, nq) - 1);
-    const int n_steps = (wg_end + WIDE_STEP - 1) / WIDE_STEP;
+    int t_full, t_hi, wave_end, n_steps;   // every column of the wave sees keys below t_full; this column's keys
+                                           // are [0, t_hi); the wave's below wave_end; the workgroup's n_steps steps
+    if constexpr (MODE == WIDE_PREFIX) {
+        // each column's own sequence caps it: its row's causal limit, within the prefix
+        int lim = 0;
+        if (wave_on) {
+            const int r_last = min(i0 + R, nq) - 1;
+            int sj = wide_seq_of_row(P, i0);
+            for (int s2 = sj + 1; s2 < P.num_seqs; ++s2) {
+                const int b = __builtin_amdgcn_readfirstlane(P.query_start[s2]);
+                if (b > r_last)
+                    break;
+                if (row >= b)
+                    sj = s2;
+            }
+            int c = P.ctx[sj];
+            c = c < 0 ? 0 : (c > cap ? cap : c);
+            const int qf = P.query_start[sj];
+            int n = P.query_start[sj + 1] - qf;
+            n = n > P.total_q - qf ? P.total_q - qf : n;
+            const int t = c - n + (row - qf) + 1;
+            lim = t < 0 ? 0 : (t > c ? c : t);
+        }
+        const int mine = on ? (lim < prefix_tok ? lim : prefix_tok) : prefix_tok;
+        t_full = wide_wave_min(mine);
+        t_hi = on ? mine : t_full;
+        wave_end = wave_on ? wide_wave_max(on ? mine : 0) : 0;
+        n_steps = (prefix_tok + WIDE_STEP - 1) / WIDE_STEP;
+    } else {
+        t_full = limit(i0);
+        t_hi = on ? limit(row) : t_full;
+        wave_end = wave_on ? limit(min(i0 + R, nq) - 1) : 0;
+        const int wg_end = limit(min(i0g + WIDE_WAVES * R, nq) - 1);
+        n_steps = (wg_end + WIDE_STEP - 1) / WIDE_STEP;
+    }
+    // WIDE_OWN: the keys below the prefix are the prefix pass's; the first step holds its last ones
+    const int t_lo = MODE == WIDE_OWN ? prefix_tok : 0;
+    const int s_first = t_lo / WIDE_STEP;
 
     const int kvh = hg / P.group_split;
     const int qh0 = kvh * P.group + (hg - kvh * P.group_split) * gh;
@@ -240,8 +327,8 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         const unsigned char PA_LDS *stg = lds + ST * WIDE_STAGE;
         // (a negative scale also takes the masked path: the other one takes the
         // max of the raw scores)
-        const bool masked =
-            t0 + WIDE_STEP > t_full || t0 + WIDE_STEP > ctx || okm != (1u << NE) - 1u || !(sl2 >= 0.f);
+        const bool masked = t0 + WIDE_STEP > t_full || t0 + WIDE_STEP > ctx || okm != (1u << NE) - 1u ||
+                            !(sl2 >= 0.f) || (MODE == WIDE_OWN && t0 < t_lo);
 
         // all sixteen K fragments of the step are requested before the first
         // product: the reads' latency is paid once per step, not per product
@@ -274,7 +361,7 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
                 for (int v = 0; v < 16; ++v) {
                     const int kr = 32 * kt + 8 * (v >> 2);             // first key of the 8-key group
                     const int key = t0 + kr + 4 * h + (v & 3);
-                    const bool ok = ((okm >> (kr / BS)) & 1u) && key < t_hi;
+                    const bool ok = ((okm >> (kr / BS)) & 1u) && key < t_hi && (MODE != WIDE_OWN || key >= t_lo);
                     sc[kt][v] = ok ? sc[kt][v] * sl2 : -INFINITY;
                 }
             mx = -INFINITY;
@@ -383,13 +470,13 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
             fetch(step + 2, ent_b);
     };
 
-    if (n_steps > 0) {
-        fetch(0, ent_a);
-        if (n_steps > 1)
-            fetch(1, ent_b);
-        issue(0, 0, ent_a);
+    if (n_steps > s_first) {
+        fetch(s_first, ent_a);
+        if (n_steps > s_first + 1)
+            fetch(s_first + 1, ent_b);
+        issue(s_first, 0, ent_a);
     }
-    for (int step = 0; step < n_steps; step += 2) {
+    for (int step = s_first; step < n_steps; step += 2) {
         run_step(step, std::integral_constant<int, 0>());
         if (step + 1 < n_steps)
             run_step(step + 1, std::integral_constant<int, 1>());
@@ -405,9 +492,46 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     }
     if (!on)
         return;
+    const int64_t col = (int64_t)(q_first + row) * P.num_q_heads + qh0 + j % gh;   // (q row, q head)
+    if constexpr (MODE == WIDE_PREFIX) {
+        // the prefix's partial of the column: (reference max, sum, unnormalised output)
+        float *ap = P.ws_acc + col * D + 4 * h;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<float4 *>(ap + 32 * dt + 8 * g) =
+                    make_float4(acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]);
+        if (h == 0)
+            P.ws_ml[col] = make_float2(m, lp);
+        return;
+    }
+    if constexpr (MODE == WIDE_OWN) {
+        // merge the prefix pass's partial of the column
+        const float2 mlp = P.ws_ml[col];
+        const float *ap = P.ws_acc + col * D + 4 * h;
+        float4 pa[4][4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                pa[dt][g] = *reinterpret_cast<const float4 *>(ap + 32 * dt + 8 * g);
+        const float mm = fmaxf(m, mlp.x);
+        const float a = fast_exp2(m - mm), b = fast_exp2(mlp.x - mm);
+        lp = lp * a + mlp.y * b;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                acc[dt][4 * g] = acc[dt][4 * g] * a + pa[dt][g].x * b;
+                acc[dt][4 * g + 1] = acc[dt][4 * g + 1] * a + pa[dt][g].y * b;
+                acc[dt][4 * g + 2] = acc[dt][4 * g + 2] * a + pa[dt][g].z * b;
+                acc[dt][4 * g + 3] = acc[dt][4 * g + 3] * a + pa[dt][g].w * b;
+            }
+    }
     const float inv = lp > 0.f ? 1.f / lp : 0.f;
     char *op = static_cast<char *>(P.out) +
-               (((int64_t)(q_first + row) * P.num_q_heads + qh0 + j % gh) * D + 4 * h) * ES;
+               (col * D + 4 * h) * ES;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -428,18 +552,34 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         }
 }
 
-template <typename T, int BS>
+// WIDE_PREFIX: one virtual sequence of p.total_q rows (max_query_len unused)
+template <typename T, int BS, int MODE = WIDE_PLAIN>
 hipError_t launch_prefill_wide(const DecodeParams &p, int max_query_len, hipStream_t st)
 {
     const int rows = WIDE_COLS / (p.group / p.group_split);
     const int per_wg = WIDE_WAVES * rows;
-    const int col_groups = (max_query_len + per_wg - 1) / per_wg;
-    const long long total = (long long)col_groups * p.num_kv_heads * p.group_split * p.num_seqs;
+    const int n_rows = MODE == WIDE_PREFIX ? p.total_q : max_query_len;
+    const int col_groups = (n_rows + per_wg - 1) / per_wg;
+    const long long total =
+        (long long)col_groups * p.num_kv_heads * p.group_split * (MODE == WIDE_PREFIX ? 1 : p.num_seqs);
     if (total > (1LL << 30))
         return hipErrorInvalidValue;
+    if (total == 0)
+        return hipSuccess;
     const dim3 grid((unsigned)((total + 7) / 8 * 8));
-    hipLaunchKernelGGL((prefill_wide_kernel<T, BS>), grid, dim3(WIDE_WAVES * 64), 0, st, p, col_groups, (int)total);
+    hipLaunchKernelGGL((prefill_wide_kernel<T, BS, MODE>), grid, dim3(WIDE_WAVES * 64), 0, st, p, col_groups,
+                       (int)total);
     return hipGetLastError();
+}
+
+// the shared-prefix form: the prefix pass over all rows, then each sequence's own keys
+template <typename T, int BS>
+hipError_t launch_prefill_shared_wide(const DecodeParams &p, int max_query_len, hipStream_t st)
+{
+    const hipError_t e = launch_prefill_wide<T, BS, WIDE_PREFIX>(p, max_query_len, st);
+    if (e != hipSuccess)
+        return e;
+    return launch_prefill_wide<T, BS, WIDE_OWN>(p, max_query_len, st);
 }
 
 }  // namespace pa

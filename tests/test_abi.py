@@ -256,6 +256,47 @@ def test_prefill_checks_arguments_first(kw, status):
     assert _prefill(**kw) == status
 
 
+def _prefill_shared(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, S=2, TQ=10, MQ=8, Hq=8, Hkv=2, D=128,
+             bs=16, MB=8, NB=32, P=4, scale=0.125, dt=B.PA_F16, layout=B.PA_LAYOUT_BHTD, ws=None, wsb=0)
+    a.update(kw)
+    return B.lib().pa_prefill_shared_prefix(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["S"],
+                                            a["TQ"], a["MQ"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"],
+                                            a["P"], a["scale"], a["dt"], a["layout"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=0), B.PA_OK), (dict(TQ=0), B.PA_OK), (dict(MQ=0), B.PA_OK),
+    (dict(P=-1), B.PA_ERR_INVALID_ARG), (dict(P=9), B.PA_ERR_INVALID_ARG),
+    (dict(TQ=-1), B.PA_ERR_INVALID_ARG), (dict(qs=None), B.PA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), B.PA_ERR_INVALID_ARG), (dict(NB=0), B.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), B.PA_ERR_INVALID_ARG), (dict(Hq=6, Hkv=4), B.PA_ERR_INVALID_ARG),
+    (dict(dt=B.PA_F32), B.PA_ERR_UNSUPPORTED), (dict(D=64), B.PA_ERR_UNSUPPORTED),
+    (dict(Hq=40, Hkv=2), B.PA_ERR_UNSUPPORTED), (dict(layout=5), B.PA_ERR_UNSUPPORTED),
+    (dict(), B.PA_ERR_WORKSPACE), (dict(ws=FAKE, wsb=10 * 8 * 520 - 1), B.PA_ERR_WORKSPACE),
+    (dict(ws=FAKE + 4, wsb=1 << 20), B.PA_ERR_WORKSPACE),
+])
+def test_prefill_shared_prefix_checks_arguments_first(kw, status):
+    # every check runs before anything touches the device
+    assert _prefill_shared(**kw) == status
+
+
+def test_prefill_shared_prefix_workspace_query():
+    sz = ctypes.c_size_t(0)
+    L = B.lib()
+    assert L.pa_prefill_shared_prefix_workspace_bytes(100, 8, 128, 16, 4, ctypes.byref(sz)) == B.PA_OK
+    # a (max, sum) pair, 256-byte aligned, then 128 floats per (row, q head)
+    assert sz.value == (100 * 8 * 8 + 255) // 256 * 256 + 100 * 8 * 128 * 4
+    # computed as pa_prefill (no workspace): no prefix, less than one 64-token step of it, no rows, head_dim 256
+    for args in ((100, 8, 128, 16, 0), (100, 8, 128, 16, 3), (100, 8, 128, 8, 7), (0, 8, 128, 16, 4),
+                 (100, 8, 256, 16, 4)):
+        assert L.pa_prefill_shared_prefix_workspace_bytes(*args, ctypes.byref(sz)) == B.PA_OK and sz.value == 0
+    assert L.pa_prefill_shared_prefix_workspace_bytes(100, 8, 96, 16, 4, ctypes.byref(sz)) == B.PA_ERR_UNSUPPORTED
+    assert L.pa_prefill_shared_prefix_workspace_bytes(100, 8, 128, 12, 4, ctypes.byref(sz)) == B.PA_ERR_UNSUPPORTED
+    assert L.pa_prefill_shared_prefix_workspace_bytes(-1, 8, 128, 16, 4, ctypes.byref(sz)) == B.PA_ERR_INVALID_ARG
+    assert L.pa_prefill_shared_prefix_workspace_bytes(100, 8, 128, 16, 4, None) == B.PA_ERR_INVALID_ARG
+
+
 def _shared(**kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, S=2, Hq=8, Hkv=2, D=128, bs=16, MB=8, NB=32, P=3,
              scale=0.125, dt=B.PA_F16, layout=B.PA_LAYOUT_BHTD, ws=None, wsb=0)

@@ -1,0 +1,126 @@
+"""GPU parity of the shared-prefix prefill (pa_prefill_shared_prefix) with the
+fp64 oracle's plain prefill (oracle/prefill.py) of every sequence over its own
+table: requests admitted onto a cached prompt (each chunk's rows past the
+shared prefix), chunks that start inside the prefix, contexts shorter than
+the prefix, empty contexts and zero-row sequences, rows with no token to
+attend, every block size, both dtypes, group shapes from MHA to 32 q heads
+per kv head, prefixes shorter than the 64-token step the passes split at or
+ending inside one; with no prefix, and at head_dim 256, the call is
+pa_prefill to the bit; a workload at the prefix-cache benchmark's scale."""
+import numpy as np
+import pytest
+import torch
+
+from oracle.prefill import paged_prefill
+from paged_kv_cache_405_amd import binding as B
+from paged_kv_cache_405_amd import workloads as W
+from tests.pa_harness import assert_close, compare, log, to_dev, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _starts(counts):
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def _run(w, g, q_np, counts, prefix_blocks):
+    qs = torch.from_numpy(_starts(counts)).cuda()
+    q = to_dev(q_np, w.dtype)
+    out = torch.full_like(q, float("nan"))
+    B.pa_prefill_shared_prefix(out, q, g.k_cache, g.v_cache, g.tables, g.ctx, qs, max(max(counts), 1), w.scale,
+                               prefix_blocks, layout=g.layout, num_blocks=w.num_blocks)
+    torch.cuda.synchronize()
+    return out, q, qs
+
+
+def _ref(w, q_np, counts):
+    return paged_prefill(q_np, w.k_cache, w.v_cache, w.block_tables, w.context_lens, _starts(counts), w.scale,
+                         w.dtype)
+
+
+def _shapes():
+    out = []
+    for dtype in ("f16", "bf16"):
+        for bs in (8, 16, 32):
+            for Hq, Hkv in ((8, 8), (16, 4), (64, 8), (32, 1)):
+                out.append((dtype, bs, Hq, Hkv))
+    return out
+
+
+@pytest.mark.parametrize("dtype,bs,Hq,Hkv", _shapes())
+@pytest.mark.parametrize("P", [1, 5, 13, 24])   # prefixes under one 64-token step, ending inside one, whole
+def test_matches_the_oracle(dtype, bs, Hq, Hkv, P):
+    pt = P * bs
+    # (context, rows): row 0 holds the whole prefix; admitted requests (rows past the prefix), a chunk that
+    # starts inside the prefix, a context shorter than the prefix, an empty context, a zero-row sequence,
+    # more rows than context, one row
+    seqs = [(pt + 37, 37), (pt + 5, 5), (pt + 70, 70), (pt + 40, 60), (max(1, pt // 2), max(1, pt // 4)),
+            (0, 3), (pt + 9, 0), (4, 9), (pt + 1, 1), (pt + 130, 130)]
+    ctxs = [c for c, _ in seqs]
+    counts = [n for _, n in seqs]
+    w = W.custom(f"psp_{dtype}_{bs}_{Hq}x{Hkv}_P{P}", dtype, ctxs, Hq, Hkv, 128, bs, seed=P * 11 + bs + Hq,
+                 append=False, table_pad=1, shared_prefix_blocks=P)
+    rng = np.random.default_rng(P * 5 + Hq + bs)
+    q_np = W.to_storage(rng.standard_normal((sum(counts), Hq, 128), dtype=np.float32), dtype)
+    g = upload(w)
+    log(f"[gpu] {w.name}")
+    out, _, _ = _run(w, g, q_np, counts, P)
+    assert_close(compare(out, _ref(w, q_np, counts), dtype), dtype, w.name)
+    assert not torch.isnan(out).any()
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_without_a_prefix_or_at_head_dim_256_it_is_pa_prefill(D):
+    w = W.custom(f"psp_plain_{D}", "bf16", [200, 70, 3], 16, 2, D, 16, seed=D, append=False, table_pad=1,
+                 shared_prefix_blocks=4)
+    counts = [64, 70, 3]
+    rng = np.random.default_rng(D + 1)
+    q_np = W.to_storage(rng.standard_normal((sum(counts), 16, D), dtype=np.float32), "bf16")
+    g = upload(w)
+    for P in ([0] if D == 128 else [0, 4]):
+        out, q, qs = _run(w, g, q_np, counts, P)
+        plain = torch.empty_like(q)
+        B.pa_prefill(plain, q, g.k_cache, g.v_cache, g.tables, g.ctx, qs, max(counts), w.scale,
+                     layout=g.layout, num_blocks=w.num_blocks)
+        torch.cuda.synchronize()
+        assert torch.equal(out, plain)
+    assert_close(compare(out, _ref(w, q_np, counts), "bf16"), "bf16", f"head_dim {D}")
+
+
+def test_prefix_cache_scale():
+    # the prefix-cache benchmark's shape, fewer requests: a 1504-token cached prompt (94 blocks) and 8-200
+    # own rows per request, 32 x 128 MHA heads, f16; the 8 q rows checked per request span the chunk
+    rng = np.random.default_rng(5)
+    own = rng.integers(8, 201, 24)
+    P, bs = 94, 16
+    ctxs = [P * bs + int(n) for n in own]
+    w = W.custom("psp_prefix_cache", "f16", ctxs, 32, 32, 128, bs, seed=6, append=False, table_pad=0,
+                 shared_prefix_blocks=P)
+    counts = [int(n) for n in own]
+    q_np = W.to_storage(rng.standard_normal((sum(counts), 32, 128), dtype=np.float32), "f16")
+    g = upload(w)
+    out, _, _ = _run(w, g, q_np, counts, P)
+    assert_close(compare(out, _ref(w, q_np, counts), "f16"), "f16", w.name)
+
+
+def test_workspace_and_argument_errors():
+    w = W.custom("psp_err", "f16", [100, 40], 8, 8, 128, 16, seed=3, append=False, shared_prefix_blocks=4)
+    counts = [10, 4]
+    q_np = W.to_storage(np.ones((sum(counts), 8, 128), dtype=np.float32), "f16")
+    g = upload(w)
+    q = to_dev(q_np, "f16")
+    qs = torch.from_numpy(_starts(counts)).cuda()
+    out = torch.empty_like(q)
+    need = B.pa_prefill_shared_prefix_workspace_bytes(sum(counts), 8, 128, 16, 4)
+    assert need >= sum(counts) * 8 * (8 + 4 * 128)
+    assert B.pa_prefill_shared_prefix_workspace_bytes(sum(counts), 8, 128, 16, 0) == 0
+    assert B.pa_prefill_shared_prefix_workspace_bytes(sum(counts), 8, 256, 16, 4) == 0
+    short = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.PaError) as e:
+        B.pa_prefill_shared_prefix(out, q, g.k_cache, g.v_cache, g.tables, g.ctx, qs, 10, w.scale, 4,
+                                   num_blocks=w.num_blocks, workspace=short)
+    assert e.value.status == B.PA_ERR_WORKSPACE
+    with pytest.raises(B.PaError) as e:
+        B.pa_prefill_shared_prefix(out, q, g.k_cache, g.v_cache, g.tables, g.ctx, qs, 10, w.scale,
+                                   w.block_tables.shape[1] + 1, num_blocks=w.num_blocks)
+    assert e.value.status == B.PA_ERR_INVALID_ARG
