@@ -951,7 +951,7 @@ const char *pa_status_string(pa_status status)
     }
 }
 
-int pa_abi_version(void) { return 202; }
+int pa_abi_version(void) { return 203; }
 
 }  // extern "C"
 

@@ -42,7 +42,7 @@ def test_status_strings_and_version(L):
         s = B.pa_status_string(code)
         assert isinstance(s, str) and s
     assert B.pa_status_string(99) == "unknown status"
-    assert B.pa_abi_version() == 202
+    assert B.pa_abi_version() == 203
 
 
 def _ws(S=4, Hq=8, Hkv=2, D=128, bs=16, MB=64, dt=B.PA_F16, pt=0):
