@@ -10,10 +10,10 @@
   block size 16.  The GPU computes the whole batch; the oracle checks every
   row of a sample of sequences (first, middle, last), each sequence's blocks
   copied into a small pool so the oracle decodes only what it reads.
-- `pa_prefill` at the shape of the prefix-cache call `bench.py --op
-  prefix_cache` times: 127 requests whose tables start with the same 94
-  blocks (a 1504-token system prompt) and whose 8-200 own tokens are the
-  query rows.
+- `pa_prefill`, and `pa_prefill_shared_prefix` (the call the benchmark
+  times), at the shape of the prefix-cache call `bench.py --op prefix_cache`:
+  127 requests whose tables start with the same 94 blocks (a 1504-token
+  system prompt) and whose 8-200 own tokens are the query rows.
 
 Pages: "vLLM 与 PagedAttention" section 二 ("注意力计算改造": the decode
 call), section 四 (prefix caching) and section 六 ("关键的工程优化":
@@ -94,7 +94,7 @@ def test_prefill_at_the_benchmarked_shape():
     _check_sample(w, q_np, counts, out, [0, S // 2, S - 1], "prefill 16 x 512 over 1536")
 
 
-def test_prefill_at_the_prefix_cache_call_shape():
+def _prefix_cache_call(shared):
     """127 requests after the first: each attends the 94 shared blocks plus its
     own 8-200 tokens, whose rows are the query rows (the cache supplied the rest)."""
     S, H, D, bs, prefix_blocks = 127, 32, 128, 16, 94
@@ -109,10 +109,25 @@ def test_prefill_at_the_prefix_cache_call_shape():
     q = to_dev(q_np, "f16")
     out = torch.full_like(q, float("nan"))
     qs = torch.from_numpy(np.concatenate([[0], np.cumsum(own)]).astype(np.int32)).cuda()
-    log(f"[gpu] prefill at the prefix-cache call shape: {S} requests, {int(own.sum())} rows")
-    B.pa_prefill(out, q, g.k_cache, g.v_cache, g.tables, g.ctx, qs, int(own.max()), w.scale,
-                 num_blocks=w.num_blocks)
+    log(f"[gpu] prefill at the prefix-cache call shape ({'shared prefix' if shared else 'per request'}): "
+        f"{S} requests, {int(own.sum())} rows")
+    if shared:
+        B.pa_prefill_shared_prefix(out, q, g.k_cache, g.v_cache, g.tables, g.ctx, qs, int(own.max()), w.scale,
+                                   prefix_blocks, num_blocks=w.num_blocks)
+    else:
+        B.pa_prefill(out, q, g.k_cache, g.v_cache, g.tables, g.ctx, qs, int(own.max()), w.scale,
+                     num_blocks=w.num_blocks)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all(), "rows left unwritten or non-finite"
     short, long_ = int(np.argmin(own)), int(np.argmax(own))
-    _check_sample(w, q_np, own, out, sorted({0, short, long_, S // 2, S - 1}), "prefix-cache call shape")
+    _check_sample(w, q_np, own, out, sorted({0, short, long_, S // 2, S - 1}),
+                  "prefix-cache call shape" + (", shared prefix" if shared else ""))
+
+
+def test_prefill_at_the_prefix_cache_call_shape():
+    _prefix_cache_call(False)
+
+
+def test_shared_prefix_prefill_at_the_prefix_cache_call_shape():
+    """pa_prefill_shared_prefix, the call the prefix-cache benchmark times, on the same inputs."""
+    _prefix_cache_call(True)
