@@ -2,9 +2,10 @@
 library's C ABI calls) and replayed several times, with eager work between
 the replays (new queries written, the output poisoned, a synchronisation):
 every replay matches an eager call on the same inputs bit for bit, and the
-first, on the seeded inputs, matches the oracle.  The library allocates
-nothing and synchronises nothing inside a call, so the capture holds only
-its kernels."""
+first, on the seeded inputs, matches the oracle.  The same for the
+shared-prefix decode and the shared-prefix prefill (two launches each, a
+workspace between them).  The library allocates nothing and synchronises
+nothing inside a call, so the capture holds only its kernels."""
 import numpy as np
 import pytest
 import torch
@@ -62,3 +63,69 @@ def test_graph_replays_match_eager(shape, pt):
         assert torch.equal(out_graph, out_eager), f"replay {i} differs from the eager call"
         if i == 0:
             assert_close(compare(out_graph, oracle_step(w), dtype), dtype, f"{w.name} pt={pt} replay 0")
+
+
+def _replay_check(step, outs, qbuf, name):
+    """capture step(out_graph), replay four times with new queries written, the
+    output poisoned and a synchronisation between the replays; every replay
+    must equal the eager call on the same inputs bit for bit"""
+    out_graph, out_eager = outs
+    step(out_eager, eager=True)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(out_graph, eager=False)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(45)
+    for i in range(4):
+        if i > 0:
+            qbuf.copy_(torch.randn(tuple(qbuf.shape), generator=gen, device="cuda", dtype=qbuf.dtype))
+        out_graph.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(out_eager, eager=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out_graph, out_eager), f"{name}: replay {i} differs from the eager call"
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("f16", 8, 8), ("bf16", 32, 4)])
+def test_shared_prefix_decode_graph(dtype, Hq, Hkv):
+    P = 6
+    ctxs = [P * 16 + 37, 40, P * 16, P * 16 + 300, 0, 1000]
+    w = W.custom(f"graph_sp_{dtype}_{Hq}x{Hkv}", dtype, ctxs, Hq, Hkv, 128, 16, seed=50 + Hq, table_pad=1,
+                 shared_prefix_blocks=P)
+    g = upload(w)
+    code = {"f16": B.PA_F16, "bf16": B.PA_BF16}[dtype]
+    nbytes = B.pa_decode_shared_prefix_workspace_bytes(len(ctxs), Hq, Hkv, 128, 16, w.max_blocks_per_seq, code, P)
+    ws = {True: torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+          False: torch.empty(nbytes, dtype=torch.uint8, device="cuda")}
+    qbuf = g.q.clone()
+
+    def step(out, eager):
+        B.pa_decode_shared_prefix(out, qbuf, g.k_cache, g.v_cache, g.tables, g.ctx, w.scale, P,
+                                  num_blocks=w.num_blocks, layout=g.layout, workspace=ws[eager])
+
+    _replay_check(step, (torch.empty_like(qbuf), torch.empty_like(qbuf)), qbuf, w.name)
+
+
+def test_shared_prefix_prefill_graph():
+    P, bs = 8, 16
+    seqs = [(P * bs + 60, 60), (P * bs + 9, 9), (P * bs + 130, 130), (P * bs - 20, 40)]
+    w = W.custom("graph_psp", "f16", [c for c, _ in seqs], 16, 4, 128, bs, seed=52, append=False, table_pad=1,
+                 shared_prefix_blocks=P)
+    g = upload(w)
+    counts = [n for _, n in seqs]
+    qs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    rng = np.random.default_rng(53)
+    qbuf = torch.from_numpy(W.to_storage(rng.standard_normal((sum(counts), 16, 128), dtype=np.float32),
+                                         "f16")).cuda()
+    nbytes = B.pa_prefill_shared_prefix_workspace_bytes(sum(counts), 16, 128, bs, P)
+    ws = {True: torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+          False: torch.empty(nbytes, dtype=torch.uint8, device="cuda")}
+
+    def step(out, eager):
+        B.pa_prefill_shared_prefix(out, qbuf, g.k_cache, g.v_cache, g.tables, g.ctx, qs, max(counts), w.scale, P,
+                                   num_blocks=w.num_blocks, layout=g.layout, workspace=ws[eager])
+
+    _replay_check(step, (torch.empty_like(qbuf), torch.empty_like(qbuf)), qbuf, w.name)
