@@ -42,6 +42,15 @@
 // memory holds -- NaN included -- never reaches the accumulators.  f16 rounds P once and the
 // running sum adds the rounded values (v_dot2_f32_f16); bf16 keeps P as
 // hi + lo in two products.
+//
+// Shared prefix ("vLLM 与 PagedAttention" section 四, prefix caching: requests
+// that reuse a cached prompt point at its blocks).  The same kernel in two
+// launches: WIDE_PREFIX takes the whole steps inside the shared prefix once,
+// with the rows of every sequence packed as the columns (each capped at its
+// own causal limit) and writes each column's (reference max, sum,
+// unnormalised output); WIDE_OWN then runs each sequence from that split on
+// and merges the column's partial before normalising.  Merging two online-
+// softmax partials is exact up to rounding, as for split-K decode.
 #pragma once
 
 #include <type_traits>
@@ -119,9 +128,10 @@ __device__ __forceinline__ int wide_wave_max(int x) {
 static __device__ __attribute__((aligned(16))) const uint4 wide_zero = {0u, 0u, 0u, 0u};
 
 // MODE: WIDE_PLAIN, WIDE_PREFIX or WIDE_OWN (above).  The shared prefix holds
-// P.part_base_blocks blocks: in WIDE_PREFIX the keys are those blocks of table
-// row 0 and one virtual sequence holds all total_q rows, each column capped at
-// its own sequence's causal limit; in WIDE_OWN the keys start past the prefix.
+// P.part_base_blocks blocks, split at its last whole step: in WIDE_PREFIX the
+// keys are the tokens below the split (table row 0) and one virtual sequence
+// holds all total_q rows, each column capped at its own sequence's causal
+// limit; in WIDE_OWN each sequence's keys start at the split.
 template <typename T, int BS, int MODE>
 __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_wide_kernel(
     const DecodeParams P, int col_groups, int total_wg)
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         const int wg_end = limit(min(i0g + WIDE_WAVES * R, nq) - 1);
         n_steps = (wg_end + WIDE_STEP - 1) / WIDE_STEP;
     }
-    // WIDE_OWN: the keys below the prefix are the prefix pass's; the first step holds its last ones
+    // WIDE_OWN: the keys below the split are the prefix pass's (the split is a step boundary)
     const int t_lo = MODE == WIDE_OWN ? prefix_tok : 0;
     const int s_first = t_lo / WIDE_STEP;
 
