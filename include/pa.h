@@ -286,10 +286,11 @@ pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *
  * automatic prefix caching, which point at the cached blocks of a shared
  * prompt ("vLLM 与 PagedAttention" section 四, the shared system prompt;
  * "指南", "Copy-on-Write：Prefix Caching 的基础").  The same function: row i of
- * sequence s attends tokens 0 .. L - n + i of its own history.  The prefix's
- * K/V are read once for the whole batch -- the rows of every sequence are the
- * columns of one matrix-core pass over them, each capped at its own causal
- * limit -- and each sequence then reads its keys past the prefix and merges.
+ * sequence s attends tokens 0 .. L - n + i of its own history.  Each sequence
+ * first reads its keys past the prefix; then the prefix's K/V are read once
+ * for the whole batch -- the rows of every sequence are the columns of one
+ * matrix-core pass over them, each capped at its own causal limit -- which
+ * merges the two and writes the rows.
  *
  *   prefix_blocks   0 .. max_blocks_per_seq: row 0 of block_tables lists the
  *                   prefix's blocks in its first prefix_blocks entries (those
@@ -299,9 +300,9 @@ pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *
  *   workspace       device memory, 16-byte aligned, at least
  *                   pa_prefill_shared_prefix_workspace_bytes(total_q,
  *                   num_q_heads, head_dim, block_size, prefix_blocks) bytes
- *                   (content on entry does not matter): the prefix's partial
- *                   result of every (row, q head), (8 + 4 head_dim) bytes
- *                   each; may be null when that size is 0
+ *                   (content on entry does not matter): the partial result
+ *                   past the prefix of every (row, q head), (8 + 4 head_dim)
+ *                   bytes each; may be null when that size is 0
  *   other arguments as for pa_prefill (no flags)
  *
  * The keys read once for every row are the whole 64-token steps inside the

@@ -305,6 +305,7 @@ struct DecodeParams {
     int order_rows;           // grid kernels: 1 = take sequences longest first (seq_of_row), 0 = in order
     const int32_t *query_start;   // multi-token calls: [num_seqs + 1] first q row of each sequence
     int total_q;                  // multi-token calls: rows of q and out
+    int own_rows;                 // shared-prefix prefill: the rows of each sequence its own pass computes
     uint64_t *stream_total;   // [1] steps of the whole stream (T), written by the stream kernel
     int32_t *unit_first;      // [HG * S] first piece of each unit, -1 when one wave finished it
     int32_t *unit_last;       // [HG * S] last piece of each cut unit

@@ -45,12 +45,14 @@
 //
 // Shared prefix ("vLLM 与 PagedAttention" section 四, prefix caching: requests
 // that reuse a cached prompt point at its blocks).  The same kernel in two
-// launches: WIDE_PREFIX takes the whole steps inside the shared prefix once,
-// with the rows of every sequence packed as the columns (each capped at its
-// own causal limit) and writes each column's (reference max, sum,
-// unnormalised output); WIDE_OWN then runs each sequence from that split on
-// and merges the column's partial before normalising.  Merging two online-
-// softmax partials is exact up to rounding, as for split-K decode.
+// launches: WIDE_OWN runs each sequence from the last whole step inside the
+// shared prefix on and writes each (row, q head)'s (reference max, sum,
+// unnormalised output); WIDE_PREFIX then takes the steps below that split
+// once, with the rows of every sequence packed as the columns (each capped at
+// its own causal limit), merges each column's partial and normalises.  The
+// long pass, whose memory is idle under its products, carries the merge's
+// loads and the output's stores.  Merging two online-softmax partials is
+// exact up to rounding, as for split-K decode.
 #pragma once
 
 #include <type_traits>
@@ -84,10 +86,11 @@ constexpr int WIDE_STAGE = 2 * WIDE_TILE;            // K then V
 constexpr int WIDE_STAGES = 2;
 constexpr float WIDE_RESCALE_LOG2 = 8.f;
 
-// what a launch computes (the shared-prefix form runs WIDE_PREFIX, then WIDE_OWN)
+// what a launch computes (the shared-prefix form runs WIDE_OWN, then WIDE_PREFIX)
 constexpr int WIDE_PLAIN = 0;    // every row over its whole causal history
-constexpr int WIDE_PREFIX = 1;   // the shared prefix only, the rows of all sequences as columns: partials out
-constexpr int WIDE_OWN = 2;      // each sequence's keys past the prefix, merged with the prefix partials
+constexpr int WIDE_PREFIX = 1;   // the shared prefix only, the rows of all sequences as columns, merged with
+                                 // the own pass's partials
+constexpr int WIDE_OWN = 2;      // each sequence's keys past the prefix: partials out
 
 // the sequence whose rows hold q row r: the largest s < num_seqs with
 // query_start[s] <= r (r wave-uniform).  Each round narrows the range with 64
@@ -131,7 +134,8 @@ static __device__ __attribute__((aligned(16))) const uint4 wide_zero = {0u, 0u, 
 // P.part_base_blocks blocks, split at its last whole step: in WIDE_PREFIX the
 // keys are the tokens below the split (table row 0) and one virtual sequence
 // holds all total_q rows, each column capped at its own sequence's causal
-// limit; in WIDE_OWN each sequence's keys start at the split.
+// limit and written only where the own pass computed the row (P.own_rows
+// rows of each sequence); in WIDE_OWN each sequence's keys start at the split.
 template <typename T, int BS, int MODE>
 __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_wide_kernel(
     const DecodeParams P, int col_groups, int total_wg)
@@ -192,6 +196,7 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     auto limit = [&](int r) { const int t = ctx - nq + r + 1; return t < 0 ? 0 : (t > ctx ? ctx : t); };
     int t_full, t_hi, wave_end, n_steps;   // every column of the wave sees keys below t_full; this column's keys
                                            // are [0, t_hi); the wave's below wave_end; the workgroup's n_steps steps
+    bool own_done = true;                  // WIDE_PREFIX: the own pass wrote this column's partial
     if constexpr (MODE == WIDE_PREFIX) {
         // each column's own sequence caps it: its row's causal limit, within the prefix
         int lim = 0;
@@ -212,6 +217,8 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
             n = n > P.total_q - qf ? P.total_q - qf : n;
             const int t = c - n + (row - qf) + 1;
             lim = t < 0 ? 0 : (t > c ? c : t);
+            // the rows the own pass computed: a sequence whose rows start inside q, the first own_rows of them
+            own_done = qf >= 0 && qf < P.total_q && row - qf < n && row - qf < P.own_rows;
         }
         const int mine = on ? (lim < prefix_tok ? lim : prefix_tok) : prefix_tok;
         t_full = wide_wave_min(mine);
@@ -503,8 +510,8 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     if (!on)
         return;
     const int64_t col = (int64_t)(q_first + row) * P.num_q_heads + qh0 + j % gh;   // (q row, q head)
-    if constexpr (MODE == WIDE_PREFIX) {
-        // the prefix's partial of the column: (reference max, sum, unnormalised output)
+    if constexpr (MODE == WIDE_OWN) {
+        // the column's partial past the split: (reference max, sum, unnormalised output)
         float *ap = P.ws_acc + col * D + 4 * h;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -516,8 +523,10 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
             P.ws_ml[col] = make_float2(m, lp);
         return;
     }
-    if constexpr (MODE == WIDE_OWN) {
-        // merge the prefix pass's partial of the column
+    if constexpr (MODE == WIDE_PREFIX) {
+        // merge the own pass's partial of the column (a row it did not compute stays as it is)
+        if (!own_done)
+            return;
         const float2 mlp = P.ws_ml[col];
         const float *ap = P.ws_acc + col * D + 4 * h;
         float4 pa[4][4];
@@ -582,14 +591,17 @@ hipError_t launch_prefill_wide(const DecodeParams &p, int max_query_len, hipStre
     return hipGetLastError();
 }
 
-// the shared-prefix form: the prefix pass over all rows, then each sequence's own keys
+// the shared-prefix form: each sequence's own keys, then the prefix pass over all rows (which merges)
 template <typename T, int BS>
 hipError_t launch_prefill_shared_wide(const DecodeParams &p, int max_query_len, hipStream_t st)
 {
-    const hipError_t e = launch_prefill_wide<T, BS, WIDE_PREFIX>(p, max_query_len, st);
+    const int per_wg = WIDE_WAVES * (WIDE_COLS / (p.group / p.group_split));
+    DecodeParams q = p;
+    q.own_rows = (max_query_len + per_wg - 1) / per_wg * per_wg;   // the rows the own pass's grid covers
+    const hipError_t e = launch_prefill_wide<T, BS, WIDE_OWN>(q, max_query_len, st);
     if (e != hipSuccess)
         return e;
-    return launch_prefill_wide<T, BS, WIDE_OWN>(p, max_query_len, st);
+    return launch_prefill_wide<T, BS, WIDE_PREFIX>(q, max_query_len, st);
 }
 
 }  // namespace pa

@@ -124,3 +124,33 @@ def test_workspace_and_argument_errors():
         B.pa_prefill_shared_prefix(out, q, g.k_cache, g.v_cache, g.tables, g.ctx, qs, 10, w.scale,
                                    w.block_tables.shape[1] + 1, num_blocks=w.num_blocks)
     assert e.value.status == B.PA_ERR_INVALID_ARG
+
+
+def test_rows_past_the_grid_stay_untouched():
+    # as pa_prefill: max_query_len sizes the grid (128-row column groups at MHA), rows past it are not written
+    P, bs = 4, 16
+    seqs = [(P * bs + 200, 200), (P * bs + 30, 30)]
+    w = W.custom("psp_grid", "f16", [c for c, _ in seqs], 8, 8, 128, bs, seed=71, append=False,
+                 shared_prefix_blocks=P)
+    counts = [n for _, n in seqs]
+    rng = np.random.default_rng(72)
+    q_np = W.to_storage(rng.standard_normal((sum(counts), 8, 128), dtype=np.float32), "f16")
+    g = upload(w)
+    q = to_dev(q_np, "f16")
+    qs = torch.from_numpy(_starts(counts)).cuda()
+    outs = {}
+    for name in ("shared", "plain"):
+        out = torch.full_like(q, 7.0)
+        if name == "shared":
+            B.pa_prefill_shared_prefix(out, q, g.k_cache, g.v_cache, g.tables, g.ctx, qs, 100, w.scale, P,
+                                       num_blocks=w.num_blocks)
+        else:
+            B.pa_prefill(out, q, g.k_cache, g.v_cache, g.tables, g.ctx, qs, 100, w.scale, num_blocks=w.num_blocks)
+        torch.cuda.synchronize()
+        outs[name] = out
+    untouched = torch.zeros(sum(counts), dtype=torch.bool, device="cuda")
+    untouched[128:200] = True
+    assert (outs["shared"][untouched] == 7.0).all() and (outs["plain"][untouched] == 7.0).all()
+    ref = _ref(w, q_np, counts)
+    keep = (~untouched).cpu().numpy()
+    assert_close(compare(outs["shared"][~untouched], ref[keep], "f16"), "f16", "rows inside the grid")
