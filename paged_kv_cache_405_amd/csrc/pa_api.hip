@@ -601,11 +601,12 @@ pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
         return PA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < pp.ws_bytes || !aligned(workspace, 16))
         return PA_ERR_WORKSPACE;
-    // Both passes go in one launch when the own blocks take the vector kernel
-    // (pa_shared_prefix.h): the prefix pass's workgroups then run beside the
-    // own-blocks pass instead of before it.
-    const bool combined = prefix_blocks > 0 && pp.max_partitions > pp.n_chunks && !pp.suffix.mfma &&
-                          (pp.suffix.gt == 1 || pp.suffix.gt == 2);
+    // Both passes go in one launch (pa_shared_prefix.h) when the own blocks
+    // take the matrix-core kernel or the vector one with 1 or 2 q heads per
+    // workgroup: the prefix pass's workgroups then run beside the own-blocks
+    // pass instead of before it.
+    const bool combined = prefix_blocks > 0 && pp.max_partitions > pp.n_chunks &&
+                          (pp.suffix.mfma || pp.suffix.gt == 1 || pp.suffix.gt == 2);
     // every argument checked (the workspace against the smallest chunk's plan,
     // as the query states it): the chunk of the call.  Beside the own-blocks
     // pass, few long chunks: fewer prefix workgroups taking room from it and
@@ -664,9 +665,10 @@ pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
         pa::DecodeParams px = p, sx = p;
         px.group_split = pp.prefix_group_split;
         sx.group_split = pp.suffix.group_split;
-        e = dtype == PA_F16 ? pa::launch_shared_prefix_f16(sx, px, head_dim, block_size, pp.suffix.gt,
+        const int gt = pp.suffix.mfma ? 0 : pp.suffix.gt;
+        e = dtype == PA_F16 ? pa::launch_shared_prefix_f16(sx, px, head_dim, block_size, gt,
                                                           prefix_blocks * block_size, pp.chunk, s)
-                            : pa::launch_shared_prefix_bf16(sx, px, head_dim, block_size, pp.suffix.gt,
+                            : pa::launch_shared_prefix_bf16(sx, px, head_dim, block_size, gt,
                                                            prefix_blocks * block_size, pp.chunk, s);
         if (e != hipSuccess)
             return PA_ERR_HIP;

@@ -14,22 +14,34 @@
 
 namespace pa {
 
+// LDS bytes of one grid workgroup of NW waves: the waves' tile slots, later
+// their merge area
+template <typename T, int D, int BS, int NW, bool STREAM_KV>
+constexpr int decode_mfma_lds()
+{
+    constexpr int MERGE_BYTES = NW * 16 * (D + 2) * 4;
+    constexpr int TILES = NW * GqaWorker<T, D, BS, STREAM_KV>::LDS_BYTES;
+    return TILES > MERGE_BYTES ? TILES : MERGE_BYTES;
+}
+
 // Grid schedule (partition_tokens != 0): one workgroup of NW waves per
 // (partition, head group, sequence); the waves take the partition's tiles
-// round robin and merge through LDS, reusing the tile slots.
+// round robin and merge through LDS, reusing the tile slots.  The workgroup
+// (partition bx of head group by of grid row bz) as a function of its block
+// coordinates, over decode_mfma_lds() bytes of LDS at `lds`: the
+// shared-prefix decode runs it inside a launch of its own (pa_shared_prefix.h).
 template <typename T, int D, int BS, int NW, bool STREAM_KV>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams P)
+__device__ __forceinline__ void decode_mfma_block(const DecodeParams &P, int bx, int by, int bz,
+                                                  unsigned char PA_LDS *lds)
 {
     static_assert(D % 128 == 0, "the grouped-query kernel needs head_dim 128 or 256");
     static_assert(BS % 8 == 0, "block size 8, 16 or 32");
     using W = GqaWorker<T, D, BS, STREAM_KV>;
-    constexpr int MERGE_BYTES = NW * 16 * (D + 2) * 4;
-    constexpr int LDS_TOTAL = NW * W::LDS_BYTES > MERGE_BYTES ? NW * W::LDS_BYTES : MERGE_BYTES;
 
-    const int p = blockIdx.x + P.first_partition;
-    const int hg = blockIdx.y;
+    const int p = bx + P.first_partition;
+    const int hg = by;
     int ctx;
-    const int s = seq_of_row(P, blockIdx.z, BS, ctx);
+    const int s = seq_of_row(P, bz, BS, ctx);
     const int nblk = (ctx + BS - 1) / BS;
     const int npart = num_partitions(P, nblk);
     if (p >= npart)
@@ -37,11 +49,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_TOTAL];
-
     W w;
     w.init_lane(lane);
-    w.init_lds((unsigned char PA_LDS *)lds + wave * W::LDS_BYTES);
+    w.init_lds(lds + wave * W::LDS_BYTES);
     w.bind(P, s, hg, ctx);
     const int gh = w.gh;
     const int qh0 = w.qh0;
@@ -60,7 +70,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     // tile slots become the merge area
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    float *sm_m = reinterpret_cast<float *>(lds);
+    float *sm_m = (float *)lds;   // the tile slots as the merge area (a generic pointer)
     float *sm_l = sm_m + NW * 16;
     float *sm_acc = sm_l + NW * 16;
     w.export_lds(sm_m + wave * 16, sm_l + wave * 16, sm_acc + wave * 16 * D);
@@ -90,6 +100,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
                 P.ws_ml[sh * P.max_partitions + p] = make_float2(M, L);
         }
     }
+}
+
+template <typename T, int D, int BS, int NW, bool STREAM_KV>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams P)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char lds[decode_mfma_lds<T, D, BS, NW, STREAM_KV>()];
+    decode_mfma_block<T, D, BS, NW, STREAM_KV>(P, blockIdx.x, blockIdx.y, blockIdx.z, (unsigned char PA_LDS *)lds);
 }
 
 constexpr int MFMA_WAVES = 4;

@@ -54,8 +54,9 @@ hipError_t launch_prefix_bf16(const DecodeParams &p, int head_dim, int block_siz
 // workgroups the prefix pass starts per chunk of the prefix
 int prefix_workgroups(int num_seqs, int group, int group_split, int num_kv_heads);
 // both passes of a shared-prefix decode in one launch (pa_shared_prefix.h):
-// `own` the own-blocks pass's parameters (vector kernel, `gt` q heads per
-// workgroup: 1 or 2), `prefix` the prefix pass's; f16 / bf16, head_dim 128 or 256
+// `own` the own-blocks pass's parameters (`gt` q heads per workgroup of the
+// vector kernel, 1 or 2, or 0 for the matrix-core kernel), `prefix` the prefix
+// pass's; f16 / bf16, head_dim 128 or 256
 hipError_t launch_shared_prefix_f16(const DecodeParams &own, const DecodeParams &prefix, int head_dim, int block_size,
                                     int gt, int prefix_tokens, int chunk, hipStream_t st);
 hipError_t launch_shared_prefix_bf16(const DecodeParams &own, const DecodeParams &prefix, int head_dim, int block_size,

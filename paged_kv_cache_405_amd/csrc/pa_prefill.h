@@ -258,17 +258,25 @@ inline int prefix_workgroups_per_chunk(int num_seqs, int group, int group_split,
     return col_groups * num_kv_heads * group_split;
 }
 
+// LDS bytes of one prefix-pass workgroup of NW waves
+template <typename T, int D, int BS, int NW>
+constexpr int prefix_block_lds()
+{
+    using PT = PrefillTiles<T, D, BS, false, NW>;
+    return PT::STAGES * PT::BYTES;
+}
+
 // One workgroup of the prefix pass (NW waves; logical workgroup lg_id of
-// total_wg): also run inside the shared-prefix decode's combined launch
-// (pa_shared_prefix.h), next to the workgroups of the own-blocks pass.
+// total_wg), over prefix_block_lds() bytes of LDS at `lds`: also run inside
+// the shared-prefix decode's combined launch (pa_shared_prefix.h), next to
+// the workgroups of the own-blocks pass, sharing their LDS.
 template <typename T, int D, int BS, int NW>
 __device__ __forceinline__ void prefix_block(const DecodeParams &P, int lg_id, int col_groups, int n_chunks,
-                                             int prefix_tokens, int chunk)
+                                             int prefix_tokens, int chunk, unsigned char PA_LDS *lds)
 {
     static_assert(D % 128 == 0, "the matrix-core worker needs head_dim 128 or 256");
     using PT = PrefillTiles<T, D, BS, false, NW>;
     using W = typename PT::W;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[PT::STAGES * PT::BYTES];
 
     const int cg = lg_id % col_groups;
     const int c = (lg_id / col_groups) % n_chunks;
@@ -287,7 +295,7 @@ __device__ __forceinline__ void prefix_block(const DecodeParams &P, int lg_id, i
     w.bind_prefix(P, hg, active ? i0 : i0g, c0, c1);
     w.reset();
     const int t_end = (c1 + GQA_TILE - 1) / GQA_TILE;
-    staged_tiles<T, D, BS, false, NW>(w, (unsigned char PA_LDS *)lds, wave, lane, c0 / GQA_TILE, t_end,
+    staged_tiles<T, D, BS, false, NW>(w, lds, wave, lane, c0 / GQA_TILE, t_end,
                                       active ? t_end : 0);
     if (active)
         w.finish_partials(P, i0, c);
@@ -302,7 +310,9 @@ __global__ __launch_bounds__(PREFIX_WAVES * 64) void prefix_kernel(const DecodeP
     const int lg_id = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
     if (lg_id >= total_wg)
         return;
-    prefix_block<T, D, BS, PREFIX_WAVES>(P, lg_id, col_groups, n_chunks, prefix_tokens, chunk);
+    __shared__ __attribute__((aligned(16))) unsigned char lds[prefix_block_lds<T, D, BS, PREFIX_WAVES>()];
+    prefix_block<T, D, BS, PREFIX_WAVES>(P, lg_id, col_groups, n_chunks, prefix_tokens, chunk,
+                                         (unsigned char PA_LDS *)lds);
 }
 
 template <typename T, int D, int BS>

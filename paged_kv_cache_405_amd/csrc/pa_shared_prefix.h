@@ -14,10 +14,12 @@
 // latency-bound walk over the prefix -- leaves most of the chip idle while it
 // runs.  Here one grid holds both: its first workgroups run the prefix pass
 // (4-wave workgroups of the same staged-tile worker), the rest run the
-// own-blocks pass of the vector decode kernel, and the hardware fills the chip
-// with whichever are ready.
+// own-blocks pass -- of the vector decode kernel, or of the matrix-core grid
+// kernel for grouped heads -- and the hardware fills the chip with whichever
+// are ready.
 #pragma once
 
+#include "pa_decode_mfma.h"
 #include "pa_decode_vec.h"
 #include "pa_prefill.h"
 
@@ -37,8 +39,12 @@ __global__ __launch_bounds__(SHARED_PREFIX_WAVES * 64) void shared_prefix_kernel
     const int b = blockIdx.x;
     if (b < n_prefix_grid) {
         const int lg_id = (b & 7) * (n_prefix_grid >> 3) + (b >> 3);
-        if (lg_id < n_prefix)
-            prefix_block<T, D, BS, SHARED_PREFIX_WAVES>(PX, lg_id, col_groups, n_chunks, prefix_tokens, chunk);
+        if (lg_id < n_prefix) {
+            __shared__ __attribute__((aligned(16)))
+            unsigned char lds[prefix_block_lds<T, D, BS, SHARED_PREFIX_WAVES>()];
+            prefix_block<T, D, BS, SHARED_PREFIX_WAVES>(PX, lg_id, col_groups, n_chunks, prefix_tokens, chunk,
+                                                        (unsigned char PA_LDS *)lds);
+        }
         return;
     }
     const int o = b - n_prefix_grid;
@@ -46,6 +52,32 @@ __global__ __launch_bounds__(SHARED_PREFIX_WAVES * 64) void shared_prefix_kernel
     decode_vec_block<T, D, BS, GT, SHARED_PREFIX_WAVES, true>(P, o % own_x, (o / own_x) % own_y, o / (own_x * own_y));
 }
 
+// the same with the own blocks on the matrix cores (grouped-query heads): the
+// grid decode kernel's workgroup (pa_decode_mfma.h) instead of the vector one
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(SHARED_PREFIX_WAVES * 64) void shared_prefix_mfma_kernel(
+    const DecodeParams P, const DecodeParams PX, int n_prefix, int n_prefix_grid, int col_groups, int n_chunks,
+    int prefix_tokens, int chunk, int own_x, int own_y)
+{
+    // a workgroup runs one of the two passes: one LDS area serves either
+    constexpr int LP = prefix_block_lds<T, D, BS, SHARED_PREFIX_WAVES>();
+    constexpr int LO = decode_mfma_lds<T, D, BS, SHARED_PREFIX_WAVES, true>();
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LP > LO ? LP : LO];
+    const int b = blockIdx.x;
+    if (b < n_prefix_grid) {
+        const int lg_id = (b & 7) * (n_prefix_grid >> 3) + (b >> 3);
+        if (lg_id < n_prefix)
+            prefix_block<T, D, BS, SHARED_PREFIX_WAVES>(PX, lg_id, col_groups, n_chunks, prefix_tokens, chunk,
+                                                        (unsigned char PA_LDS *)lds);
+        return;
+    }
+    const int o = b - n_prefix_grid;
+    decode_mfma_block<T, D, BS, SHARED_PREFIX_WAVES, true>(P, o % own_x, (o / own_x) % own_y, o / (own_x * own_y),
+                                                           (unsigned char PA_LDS *)lds);
+}
+
+// GT: q heads per workgroup of the vector own-blocks pass (1 or 2), or 0 for
+// the matrix-core own-blocks pass
 template <typename T, int D, int BS, int GT>
 hipError_t launch_shared_prefix_shape(const DecodeParams &own, const DecodeParams &px, int prefix_tokens, int chunk,
                                       hipStream_t st)
@@ -65,9 +97,14 @@ hipError_t launch_shared_prefix_shape(const DecodeParams &own, const DecodeParam
     const long long total = n_prefix_grid + own_x * own_y * own.num_seqs;
     if (own_x <= 0 || total > (1LL << 30))
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((shared_prefix_kernel<T, D, BS, GT>), dim3((unsigned)total), dim3(SHARED_PREFIX_WAVES * 64),
-                       0, st, own, px, (int)n_prefix, (int)n_prefix_grid, col_groups, n_chunks, prefix_tokens, chunk,
-                       (int)own_x, (int)own_y);
+    if constexpr (GT == 0)
+        hipLaunchKernelGGL((shared_prefix_mfma_kernel<T, D, BS>), dim3((unsigned)total),
+                           dim3(SHARED_PREFIX_WAVES * 64), 0, st, own, px, (int)n_prefix, (int)n_prefix_grid,
+                           col_groups, n_chunks, prefix_tokens, chunk, (int)own_x, (int)own_y);
+    else
+        hipLaunchKernelGGL((shared_prefix_kernel<T, D, BS, GT>), dim3((unsigned)total),
+                           dim3(SHARED_PREFIX_WAVES * 64), 0, st, own, px, (int)n_prefix, (int)n_prefix_grid,
+                           col_groups, n_chunks, prefix_tokens, chunk, (int)own_x, (int)own_y);
     return hipGetLastError();
 }
 
@@ -76,6 +113,7 @@ hipError_t launch_shared_prefix_gt(const DecodeParams &own, const DecodeParams &
                                    int chunk, hipStream_t st)
 {
     switch (gt) {
+    case 0: return launch_shared_prefix_shape<T, D, BS, 0>(own, px, prefix_tokens, chunk, st);
     case 1: return launch_shared_prefix_shape<T, D, BS, 1>(own, px, prefix_tokens, chunk, st);
     case 2: return launch_shared_prefix_shape<T, D, BS, 2>(own, px, prefix_tokens, chunk, st);
     default: return hipErrorInvalidValue;
