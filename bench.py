@@ -39,7 +39,9 @@ def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: 3; 20 for the matrix-core bound prefill "
+                         "and prefix_cache ops, whose clocks take that long to settle)")
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "llama70b_gqa", "llama70b_tp8", "mixed_bs8", "mixed_bs16", "mixed_bs32",
                              "shared_prefix", "tiny_f32"])
@@ -59,6 +61,8 @@ def parse(argv=None):
     ap.add_argument("--no-configs", action="store_true",
                     help="time only the chosen workload, not the other configurations next to it")
     ap.add_argument("--config-steps", type=int, default=5, help="timed steps of each other configuration")
+    ap.add_argument("--config-warmup", type=int, default=10,
+                    help="untimed steps before each other configuration's timed ones (the clocks settle under load)")
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
     ap.add_argument("--op", choices=["decode", "prefill", "prefix_cache", "copy_blocks", "swap_out", "swap_in"],
                     default="decode",
@@ -68,65 +72,57 @@ def parse(argv=None):
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device a few times (the known-size kernel that scales the "
                          "HBM byte counters of a profiler run) and exit")
-    return ap.parse_args(argv)
+    a = ap.parse_args(argv)
+    if a.warmup is None:
+        a.warmup = 20 if a.op in ("prefill", "prefix_cache") else 3
+    return a
 
 
 HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 MFMA_F16_PEAK_TFLOPS = 2500.0   # dense f16 / bf16 matrix-core peak of the MI355X
 
 
-def prefix_cache_step(args):
-    """Automatic prefix caching on the pages' customer-service case, at the shared-prefix workload's scale:
-    128 requests whose prompts are one 1504-token system prompt plus 8-200 tokens of their own (32 x 128 MHA
-    heads, fp16, block size 16).  The first request computes its whole prompt; then the other 127 are
-    admitted and prefilled, with the cache (the library's block manager: they reuse the 94 system-prompt
-    blocks and compute only their own tokens; pa_prefill_shared_prefix reads those blocks once for all of
-    their rows, pa_prefill per request is timed beside it) and without it (every prompt computed in full).  Host: the
-    library's manager admitting a request (pa_bm_add_cached + pa_bm_append_tokens), the oracle's model
-    beside it."""
-    import torch
-    from paged_kv_cache_405_amd import binding as B
-    from oracle.prefix_cache import PrefixCacheModel
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    B.lib()
-    S, sys_len, H, D, bs = 128, 1504, 32, 128, 16
+def prefix_cache_requests():
+    """The 128 prompts: one 1504-token system prompt plus 8-200 tokens of each request's own."""
+    S, sys_len, bs = 128, 1504, 16
     rng = np.random.default_rng(31)
     system = rng.integers(0, 32000, sys_len).astype(np.int32)
     own = rng.integers(8, 201, S)
     prompts = [np.concatenate([system, rng.integers(0, 32000, n).astype(np.int32)]) for n in own]
     NB = sum(-(-len(p) // bs) for p in prompts) + 16
     MB = max(-(-len(p) // bs) for p in prompts)
+    return prompts, NB, MB, bs
 
-    def admit(mgr, cached: bool):
-        hits, slots = [], []
-        for sid, p in enumerate(prompts):
-            hit = mgr.add_cached(sid, p) if cached else (mgr.add(sid) or 0)
-            sl, _ = mgr.append_tokens(sid, p[hit:])
-            hits.append(hit)
-            slots.append(sl)
-        return hits, slots
 
+def prefix_cache_admit(mgr, prompts, cached: bool):
+    """Admit every request into a block manager (the library's or the model), in order; returns the cache hits."""
+    hits = []
+    for sid, p in enumerate(prompts):
+        hit = mgr.add_cached(sid, p) if cached else (mgr.add(sid) or 0)
+        mgr.append_tokens(sid, p[hit:])
+        hits.append(hit)
+    return hits
+
+
+def prefix_cache_measure(torch, B, steps, warmup, host_reps=1):
+    """The GPU prefill of the 127 requests admitted after the first: with the cache and the shared-prefix call
+    ("cached"), with the cache and pa_prefill per request ("cached_plain"), without the cache ("full");
+    each call timed back to back between one pair of events.  Also the library manager's admission time."""
+    S, H, D = 128, 32, 128
+    prompts, NB, MB, bs = prefix_cache_requests()
+    dev = torch.device("cuda:0")
     # host: admitting every request (the first computes its prompt, the rest hit the cache)
-    reps = max(1, args.steps // 5)
     t = time.perf_counter()
-    for _ in range(reps):
+    for _ in range(host_reps):
         bm = B.BlockManager(NB, 0, bs)
-        hits, _ = admit(bm, True)
+        hits = prefix_cache_admit(bm, prompts, True)
         tables_c, lens_c = bm.block_tables(list(range(S)), MB)
         bm.close()
-    host_us = (time.perf_counter() - t) / reps / S * 1e6
-    t = time.perf_counter()
-    model = PrefixCacheModel(NB, 0, bs)
-    mhits, _ = admit(model, True)                  # the model on the same int32 token arrays
-    model_us = (time.perf_counter() - t) / S * 1e6
-    assert mhits == hits, "the library and the model disagree on the cache hits"
+    host_us = (time.perf_counter() - t) / host_reps / S * 1e6
     bm = B.BlockManager(NB, 0, bs)
-    admit(bm, False)
+    prefix_cache_admit(bm, prompts, False)
     tables_f, lens_f = bm.block_tables(list(range(S)), MB)
     bm.close()
-    log(f"[bench] prefix cache: {sum(h > 0 for h in hits)} of {S} requests hit, {hits[1]} tokens each; "
-        f"host {host_us:.2f} us per request (library), {model_us:.1f} us (oracle model)")
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(32)
@@ -161,23 +157,54 @@ def prefix_cache_step(args):
 
     ms = {}
     for r in runs:
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             call(r)
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             call(r)
         t1.record(stream)
         torch.cuda.synchronize()
-        ms[r] = t0.elapsed_time(t1) / args.steps
+        ms[r] = t0.elapsed_time(t1) / steps
+    del runs, kc, vc, ws
     prompt_tokens = sum(len(prompts[i]) for i in later)
     # algorithmic flops of the cached call: each computed row attends its position + 1 tokens
     flops = sum(sum(hits[i] + j + 1 for j in range(len(prompts[i]) - hits[i])) for i in later) * H * 4 * D
-    achieved = flops / (ms["cached"] * 1e-3) / 1e12
+    return {"ms": ms, "flops": flops, "achieved": flops / (ms["cached"] * 1e-3) / 1e12, "hits": hits,
+            "prompt_tokens": prompt_tokens, "tokens_from_cache": sum(hits[i] for i in later),
+            "prefix_blocks": prefix_blocks, "host_us": host_us}
+
+
+def prefix_cache_step(args):
+    """Automatic prefix caching on the pages' customer-service case, at the shared-prefix workload's scale:
+    128 requests whose prompts are one 1504-token system prompt plus 8-200 tokens of their own (32 x 128 MHA
+    heads, fp16, block size 16).  The first request computes its whole prompt; then the other 127 are
+    admitted and prefilled, with the cache (the library's block manager: they reuse the 94 system-prompt
+    blocks and compute only their own tokens; pa_prefill_shared_prefix reads those blocks once for all of
+    their rows, pa_prefill per request is timed beside it) and without it (every prompt computed in full).  Host: the
+    library's manager admitting a request (pa_bm_add_cached + pa_bm_append_tokens), the oracle's model
+    beside it."""
+    import torch
+    from paged_kv_cache_405_amd import binding as B
+    from oracle.prefix_cache import PrefixCacheModel
+    torch.cuda.set_device(torch.device("cuda:0"))
+    B.lib()
+    m = prefix_cache_measure(torch, B, args.steps, args.warmup, host_reps=max(1, args.steps // 5))
+    ms, hits, host_us, prefix_blocks = m["ms"], m["hits"], m["host_us"], m["prefix_blocks"]
+    S = len(hits)
+    prompts, NB, _, bs = prefix_cache_requests()
+    t = time.perf_counter()
+    model = PrefixCacheModel(NB, 0, bs)
+    mhits = prefix_cache_admit(model, prompts, True)        # the model on the same int32 token arrays
+    model_us = (time.perf_counter() - t) / S * 1e6
+    assert mhits == hits, "the library and the model disagree on the cache hits"
+    log(f"[bench] prefix cache: {sum(h > 0 for h in hits)} of {S} requests hit, {hits[1]} tokens each; "
+        f"host {host_us:.2f} us per request (library), {model_us:.1f} us (oracle model)")
     log(f"[bench] prefill of 127 admitted requests: {ms['cached'] * 1e3:.1f} us with the cache "
         f"({prefix_blocks} shared blocks read once for all rows; {ms['cached_plain'] * 1e3:.1f} us with pa_prefill), "
         f"{ms['full'] * 1e3:.1f} us without ({ms['full'] / ms['cached']:.1f}x)")
+    prompt_tokens = m["prompt_tokens"]
     result = {
         "metric": "prompt tokens made ready per second with automatic prefix caching (GPU prefill)",
         "value": round(prompt_tokens / (ms["cached"] * 1e-3), 1),
@@ -194,12 +221,13 @@ def prefix_cache_step(args):
         "shared_prefix_blocks": prefix_blocks,
         "prefill_us_without_cache": round(ms["full"] * 1e3, 2),
         "speedup": round(ms["full"] / ms["cached"], 2),
-        "prompt_tokens_from_cache": round(sum(hits[i] for i in later) / prompt_tokens, 4),
+        "prompt_tokens_from_cache": round(m["tokens_from_cache"] / prompt_tokens, 4),
         "host_us_per_request": round(host_us, 3),
         "roofline": {"kernel": "prefill_wide_kernel (the cached call: the shared prefix once for every row, then "
-                               "each request's own keys)", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": None, "avg_call_us": round(ms["cached"] * 1e3, 3), "flops_per_call": flops},
+                               "each request's own keys)", "bound": "mfma", "achieved": round(m["achieved"], 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(m["achieved"] / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_call_us": round(ms["cached"] * 1e3, 3), "flops_per_call": m["flops"]},
         "cpu_baseline": {"value": round(1e6 / model_us, 1), "unit": "requests admitted/s", "cores": 1,
                          "kind": "oracle", "sample": "the prefix-cache model admitting the same 128 requests "
                                                      f"({model_us:.1f} us each; the library: {host_us:.2f} us)"},
@@ -207,19 +235,16 @@ def prefix_cache_step(args):
     print(json.dumps(result), flush=True)
 
 
-def prefill_step(args):
-    """Time chunked prefill (pa_prefill) on Llama-2-7B-shaped layers: 16 sequences, each appending and
-    attending a 512-token chunk over a 1536-token cached history (context 2048), 32 x 128 MHA heads, fp16,
-    block size 16; 8 layers with their own pools."""
-    import torch
-    from paged_kv_cache_405_amd import binding as B
-    from oracle.prefill import paged_prefill
+PREFILL_SHAPE = dict(S=16, chunk=512, hist=1536, H=32, D=128, bs=16)
+
+
+def prefill_measure(torch, B, steps, warmup, layers):
+    """pa_prefill on Llama-2-7B-shaped layers, the calls back to back between one pair of events: 16 sequences,
+    each attending a 512-token chunk over a 1536-token cached history (context 2048), 32 x 128 MHA heads, fp16,
+    block size 16, `layers` layers with their own pools."""
+    S, chunk, hist, H, D, bs = (PREFILL_SHAPE[k] for k in ("S", "chunk", "hist", "H", "D", "bs"))
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    B.lib()
-    S, chunk, hist, H, D, bs = 16, 512, 1536, 32, 128, 16
     ctx = hist + chunk
-    layers = args.layers or 8
     nblk = ctx // bs
     NB = S * nblk + S * nblk // 10
     rng = np.random.default_rng(21)
@@ -244,24 +269,44 @@ def prefill_step(args):
         for kc, vc, q, out in Ls:
             B.pa_prefill(out, q, kc, vc, t_dev, ctx_dev, qs_dev, chunk, scale, stream=stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # the calls back to back between one pair of events
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for k in range(args.steps):
+    for k in range(steps):
         step()
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    call_ms = total_ms / (args.steps * layers)
+    call_ms = total_ms / (steps * layers)
     # algorithmic work: query row i of a chunk attends hist + i + 1 tokens; 2 D flops for q.k and 2 D for p.v
     attended = S * sum(hist + i + 1 for i in range(chunk))
     flops = attended * H * 4 * D
-    achieved = flops / (call_ms * 1e-3) / 1e12
+    del Ls
+    return {"total_ms": total_ms, "call_ms": call_ms, "flops": flops, "layers": layers, "steps": steps,
+            "achieved": flops / (call_ms * 1e-3) / 1e12}
+
+
+def prefill_step(args):
+    """Time chunked prefill (pa_prefill) on Llama-2-7B-shaped layers: 16 sequences, each appending and
+    attending a 512-token chunk over a 1536-token cached history (context 2048), 32 x 128 MHA heads, fp16,
+    block size 16; 8 layers with their own pools."""
+    import torch
+    from paged_kv_cache_405_amd import binding as B
+    from oracle.prefill import paged_prefill
+    torch.cuda.set_device(torch.device("cuda:0"))
+    B.lib()
+    S, chunk, hist, H, D, bs = (PREFILL_SHAPE[k] for k in ("S", "chunk", "hist", "H", "D", "bs"))
+    ctx = hist + chunk
+    nblk = ctx // bs
+    layers = args.layers or 8
+    m = prefill_measure(torch, B, args.steps, args.warmup, layers)
+    total_ms, call_ms, flops, achieved = m["total_ms"], m["call_ms"], m["flops"], m["achieved"]
     calls = args.steps * layers
+    scale = float(np.float32(1 / np.sqrt(D)))
     # the oracle, as it is, on one sequence of the same shape (K/V drawn on the host)
+    rng = np.random.default_rng(23)
     hk = fp16_storage(rng.standard_normal((nblk, bs, H, D), dtype=np.float32))
     hv = fp16_storage(rng.standard_normal((nblk, bs, H, D), dtype=np.float32))
     hq = fp16_storage(rng.standard_normal((chunk, H, D), dtype=np.float32))
@@ -804,7 +849,7 @@ def main():
             ccfg = run_config(args, cw, B)
             pool = 2 * cw.k_cache.nbytes
             layers = max(4, min(ccfg["layers"], int(np.ceil(CONFIG_POOL_BYTES / max(pool, 1)))))
-            cm = decode_run(args, cw, ccfg, layers, args.config_steps, 2, torch, B, repeats=3, warm_calls=5)
+            cm = decode_run(args, cw, ccfg, layers, args.config_steps, args.config_warmup, torch, B, repeats=3, warm_calls=5)
             configs[name] = config_entry(cw, cm)
             if not args.no_cpu_baseline:
                 # the oracle on the same workload: median of 3 shorter samples, all threads
@@ -812,6 +857,25 @@ def main():
                 configs[name]["cpu_baseline"] = {k: r[k] for k in ("value", "unit", "seq_layers_per_s", "values",
                                                                    "seconds", "threads")}
             del cw
+        # the multi-token calls at their benchmarked shapes (matrix-core bound: TFLOP/s against the f16 peak)
+        pm = prefill_measure(torch, B, max(10, args.config_steps), max(20, args.config_warmup), 8)
+        configs["prefill_7b_chunk512"] = {
+            "workload": "pa_prefill: 16 seqs x 512-token chunk over 1536 cached tokens, 32x128 MHA, fp16, bs 16",
+            "kernel": "prefill_wide_kernel", "layers": pm["layers"], "steps": pm["steps"],
+            "call_us": round(pm["call_ms"] * 1e3, 3), "flops_per_call": pm["flops"],
+            "achieved_tflops": round(pm["achieved"], 2), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
+            "frac": round(pm["achieved"] / MFMA_F16_PEAK_TFLOPS, 4)}
+        cm = prefix_cache_measure(torch, B, max(10, args.config_steps), max(20, args.config_warmup))
+        configs["prefix_cache"] = {
+            "workload": "pa_prefill_shared_prefix: the 127 requests admitted after the first onto a cached 1504-token "
+                        "system prompt (8-200 own tokens each), 32x128 MHA, fp16, bs 16",
+            "kernel": "prefill_wide_kernel (own pass, then the shared-prefix pass)", "steps": max(10, args.config_steps),
+            "call_us": round(cm["ms"]["cached"] * 1e3, 3),
+            "call_us_pa_prefill_per_request": round(cm["ms"]["cached_plain"] * 1e3, 3),
+            "call_us_without_cache": round(cm["ms"]["full"] * 1e3, 3), "flops_per_call": cm["flops"],
+            "achieved_tflops": round(cm["achieved"], 2), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
+            "frac": round(cm["achieved"] / MFMA_F16_PEAK_TFLOPS, 4),
+            "prompt_tokens_per_s": round(cm["prompt_tokens"] / (cm["ms"]["cached"] * 1e-3), 1)}
         result["configs"] = configs
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on bounded samples")

@@ -58,6 +58,16 @@ def test_default_workload_is_the_7b_shape():
     assert bench.parse([]).workload == "llama7b"
 
 
+def test_warmup_defaults():
+    """the matrix-core bound ops warm up longer by default; an explicit --warmup always wins"""
+    assert bench.parse([]).warmup == 3
+    assert bench.parse(["--op", "copy_blocks"]).warmup == 3
+    assert bench.parse(["--op", "prefill"]).warmup == 20
+    assert bench.parse(["--op", "prefix_cache"]).warmup == 20
+    assert bench.parse(["--op", "prefill", "--warmup", "2"]).warmup == 2
+    assert bench.parse(["--config-warmup", "4"]).config_warmup == 4
+
+
 def test_cpu_rates_on_a_small_workload():
     """the oracle timing helper: median of its samples, positive rates, the thread count it used"""
     w = W.tiny_f32(poison=False)
