@@ -11,26 +11,29 @@
 // A prefill reads each key for many query rows, so the work is a dense
 // product per (sequence, kv head) and wants the widest matrix tiles the
 // registers allow.  One wave owns 32 score columns -- 32 / gh query rows
-// times the gh q heads of one kv head -- and takes the keys 64 at a time:
+// times the gh q heads of one kv head -- and takes the keys 32 at a time:
 //
-//   S^T[32 keys x 32 cols] = K . Q^T     two per step, 8 products each (d = 128)
+//   S^T[32 keys x 32 cols] = K . Q^T     one per step, 8 products (d = 128)
 //       A operand K from LDS (lane l: key l % 32, dims 16c + 8(l / 32) .. +8),
 //       B operand Q held in registers for the whole kernel.  Lane l then holds
 //       column l % 32 at keys 8(v / 4) + 4(l / 32) + v % 4 of the tile, v < 16.
-//   softmax   per column: the lane and its partner l ^ 32 hold all 64 keys; the
+//   softmax   per column: the lane and its partner l ^ 32 hold all 32 keys; the
 //       reference max changes only when a step's max exceeds it by 2^8, so
 //       the accumulators are rarely rescaled.
-//   O^T[32 dims x 32 cols] += V^T . P^T  four dim tiles x four 16-key chunks
+//   O^T[32 dims x 32 cols] += V^T . P^T  four dim tiles x two 16-key chunks
 //       B operand P^T straight from the lane's own probabilities (the eight of
-//       chunk c are registers 8(c % 2) .. +8 of tile c / 2: keys 16c +
+//       chunk c are registers 8c .. +8 of the scores: keys 16c +
 //       {4h .. 4h + 3, 8 + 4h .. 8 + 4h + 3} for h = l / 32), A operand V^T
 //       read from LDS with two transposed reads (ds_read_b64_tr_b16) whose
 //       keys follow that same order.
 //
 // The four waves of a workgroup (128 columns) share each step's K and V
-// tiles, staged in LDS by direct-to-LDS loads (no registers), two steps in
-// rotation.  A tile is 64 rows of 256 bytes, written in 1 KiB pieces of four
-// rows; inside a piece, 16-byte unit u of row k sits at slot
+// tiles, staged in LDS by direct-to-LDS loads (no registers), three steps in
+// rotation, so the loads run two steps (64 keys) ahead of the products.  The
+// 48 KB of stages and 156 registers a lane let three workgroups -- three
+// waves per SIMD -- share a CU, whose other waves hide a wave's load and
+// product latencies.  A tile is 32 rows of 256 bytes, written in 1 KiB
+// pieces of four rows; inside a piece, 16-byte unit u of row k sits at slot
 // 16 (k % 4) + (u ^ s(k)) with s(k) = 4 (k % 4) + (k / 4) % 4.  Each
 // 16-lane group of a load then reads one whole 256-byte row (coalesced), the
 // K operand reads (16 rows, one unit) and the transposed V reads (4 rows x 4
@@ -80,10 +83,10 @@ template <> struct WideOps<bf16_t> {
 
 constexpr int WIDE_WAVES = 4;                        // waves per workgroup
 constexpr int WIDE_COLS = 32;                        // score columns per wave
-constexpr int WIDE_STEP = PREFILL_WIDE_STEP;         // keys per step
-constexpr int WIDE_TILE = WIDE_STEP * 256;           // bytes of K (or V) per step at head_dim 128
-constexpr int WIDE_STAGE = 2 * WIDE_TILE;            // K then V
-constexpr int WIDE_STAGES = 2;
+constexpr int WIDE_STEP = PREFILL_WIDE_STEP;         // the shared-prefix split's unit (keys)
+constexpr int WIDE_SK = 32;                          // keys per step of the kernel
+constexpr int WIDE_LDS = 3 * 2 * WIDE_SK * 256;      // LDS of the tile stages: three steps of K and V (48 KB)
+constexpr int WIDE_WAVES_PER_EU = 3;                 // three workgroups per CU (registers and LDS allow it)
 constexpr float WIDE_RESCALE_LOG2 = 8.f;
 
 // what a launch computes (the shared-prefix form runs WIDE_OWN, then WIDE_PREFIX)
@@ -137,15 +140,27 @@ static __device__ __attribute__((aligned(16))) const uint4 wide_zero = {0u, 0u, 
 // limit and written only where the own pass computed the row (P.own_rows
 // rows of each sequence); in WIDE_OWN each sequence's keys start at the split.
 template <typename T, int BS, int MODE>
-__global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_wide_kernel(
+__global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu(WIDE_WAVES_PER_EU))) void prefill_wide_kernel(
     const DecodeParams P, int col_groups, int total_wg)
 {
     constexpr int D = 128;
     constexpr int ES = 2;
     constexpr bool HILO = std::is_same<T, bf16_t>::value;
-    constexpr int NE = WIDE_STEP / BS;                 // table entries per step
+    constexpr int SK = WIDE_SK;                        // keys per step
+    static_assert(SK == 32 || SK == 64, "keys per step");
+    static_assert(WIDE_LDS % (2 * SK * 256) == 0 && WIDE_LDS / (2 * SK * 256) >= 2 && WIDE_LDS / (2 * SK * 256) <= 4,
+                  "two to four stages");
+    static_assert(WIDE_STEP % SK == 0, "the shared-prefix split is a step boundary");
+    constexpr int TILE = SK * 256;                     // bytes of K (or V) per step at head_dim 128
+    constexpr int STAGE = 2 * TILE;                    // K then V
+    constexpr int NST = WIDE_LDS / STAGE;              // stages in rotation: loads run NST - 1 steps ahead
+    constexpr int KT = SK / 32;                        // 32-key score tiles per step
+    constexpr int NCH = SK / 16;                       // 16-key chunks of the weighted sums per step
+    constexpr int PPW = SK / 8;                        // 1 KiB pieces each wave loads per step
+    constexpr int RPW = SK / 2;                        // rows of K (or V) each wave loads per step
+    constexpr int NE = SK / BS;                        // table entries per step
     static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
-    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[WIDE_STAGES * WIDE_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[NST * STAGE];
     unsigned char PA_LDS *const lds = (unsigned char PA_LDS *)lds_raw;
 
     // logical workgroups XCD-major (dispatch puts workgroup b on XCD b % 8):
@@ -224,17 +239,17 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         t_full = wide_wave_min(mine);
         t_hi = on ? mine : t_full;
         wave_end = wave_on ? wide_wave_max(on ? mine : 0) : 0;
-        n_steps = (prefix_tok + WIDE_STEP - 1) / WIDE_STEP;
+        n_steps = (prefix_tok + SK - 1) / SK;
     } else {
         t_full = limit(i0);
         t_hi = on ? limit(row) : t_full;
         wave_end = wave_on ? limit(min(i0 + R, nq) - 1) : 0;
         const int wg_end = limit(min(i0g + WIDE_WAVES * R, nq) - 1);
-        n_steps = (wg_end + WIDE_STEP - 1) / WIDE_STEP;
+        n_steps = (wg_end + SK - 1) / SK;
     }
     // WIDE_OWN: the keys below the split are the prefix pass's (the split is a step boundary)
     const int t_lo = MODE == WIDE_OWN ? prefix_tok : 0;
-    const int s_first = t_lo / WIDE_STEP;
+    const int s_first = t_lo / SK;
 
     const int kvh = hg / P.group_split;
     const int qh0 = kvh * P.group + (hg - kvh * P.group_split) * gh;
@@ -265,25 +280,26 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     }
 
     // direct loads: lane p brings row p / 16 of the piece, unit (p % 16) ^ s(row)
-    const uint32_t ld_row = (uint32_t)((lane >> 4) * tok_bytes);
-    const uint32_t ld_unit = (uint32_t)((16 * (lane & 15)) ^ (64 * (lane >> 4)));
+    // (rows are a multiple of 256 bytes apart, so piece jj's unit is ld_addr ^ 16 (jj % 4))
+    uint32_t ld_addr = (uint32_t)((lane >> 4) * tok_bytes) + (uint32_t)((16 * (lane & 15)) ^ (64 * (lane >> 4)));
     // K operand: key l % 32 of the tile, unit 2c + h
     const int kl = lane & 31;
-    const uint32_t k_base = 1024 * (kl >> 2) + 256 * (kl & 3);
-    const uint32_t k_x = (uint32_t)(h ^ (4 * (kl & 3) + ((kl >> 2) & 3)));
+    // (row offset 1024 (kl / 4) + 256 (kl % 4), unit k_x ^ 2c: byte k_addr ^ 32c of the tile)
+    uint32_t k_addr = (1024 * (kl >> 2) + 256 * (kl & 3)) | (16u * (uint32_t)(h ^ (4 * (kl & 3) + ((kl >> 2) & 3))));
     // V operand, transposed reads: source lane (group g, index i) addresses key
     // 16c + 8rho + 4h + i / 4, dims 32dt + 16(g % 2) + 4(i % 4) .. +4
     const int vi = lane & 15;
     const int vgd = (lane >> 4) & 1;
-    const uint32_t v_a = 1024 * h + 256 * (vi >> 2) + 16 * ((2 * vgd + ((vi & 3) >> 1)) ^ h) + 8 * (vi & 1);
-    const uint32_t v_b = 64 * (vi >> 2);
+    // (dim tile dt at byte v_addr ^ 64dt of a 16-key chunk, the second read at that ^ 32, 2048 on)
+    uint32_t v_addr = (1024 * h + 256 * (vi >> 2) + 16 * ((2 * vgd + ((vi & 3) >> 1)) ^ h) + 8 * (vi & 1)) | (64 * (vi >> 2));
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
     // the table entries of a step (clamped to the sequence's last block; a
     // block past it holds only rows past the context).  Each step's entries
-    // are fetched two steps ahead, so the scalar loads are never waited for.
+    // are fetched a step before its tile loads are issued, so the scalar
+    // loads have a whole step's products to land in.
     auto fetch = [&](int step, int (&ent)[NE]) {
-        const int b = step * (WIDE_STEP / BS);
+        const int b = step * NE;
         if (b + NE <= nblk) {
 #pragma unroll
             for (int e = 0; e < NE; ++e)
@@ -295,34 +311,39 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         }
     };
 
-    // step `step` into stage `st`: waves 0-1 bring K, 2-3 bring V, eight
-    // 1 KiB pieces each (rows 32 (wave % 2) + 4jj .. +4 of the step).  A row
-    // past the context or in a block outside the pool is read from 16 zero
-    // bytes instead: its K scores are masked, and its V row, all zero, adds
-    // nothing (the products never see what such memory holds)
+    // step `step` into stage `st`: waves 0-1 bring K, 2-3 bring V, PPW 1 KiB
+    // pieces each (rows RPW (wave % 2) + 4jj .. +4 of the step).  A row past
+    // the context or in a block outside the pool is read from 16 zero bytes
+    // instead: its K scores are masked, and its V row, all zero, adds nothing
+    // (the products never see what such memory holds)
     auto issue = [&](int step, int st, const int (&ent)[NE]) {
-        const int tok = step * WIDE_STEP + 32 * (wave & 1);
+        const int tok = step * SK + RPW * (wave & 1);
         const char *pool = (wave >> 1) ? vpool : kpool;
-        const uint32_t dst = lds0 + st * WIDE_STAGE + (wave >> 1) * WIDE_TILE + 8192 * (wave & 1);
-        constexpr int PER_BLK = BS / 4 < 8 ? BS / 4 : 8;   // pieces per block entry
-        constexpr int HALF = NE / 2;                       // first entry of rows 32 ..
+        const uint32_t dst = lds0 + st * STAGE + (wave >> 1) * TILE + (TILE / 2) * (wave & 1);
+        constexpr int PER_BLK = BS / 4 < PPW ? BS / 4 : PPW;   // pieces per block entry
 #pragma unroll
-        for (int e = 0; e < 8 / PER_BLK; ++e) {
-            const int lo_e = ent[e], hi_e = ent[HALF + e];      // constant indices: the array stays in registers
+        for (int g = 0; g < PPW / PER_BLK; ++g) {
+            // the entry of the group's rows in either half (constant indices: the array stays in registers)
+            const int lo_e = ent[(4 * PER_BLK * g) / BS], hi_e = ent[(RPW + 4 * PER_BLK * g) / BS];
             const int raw = (wave & 1) ? hi_e : lo_e;
+            const int row0 = (RPW * (wave & 1) + 4 * PER_BLK * g) % BS;   // the group's first row in its block
             const bool mapped = (unsigned)raw < (unsigned)num_blocks;
-            const char *blk = pool + (uint64_t)(uint32_t)(mapped ? raw : 0) * (uint64_t)blk_bytes;
-            const int t_e = tok + 4 * PER_BLK * e;             // first row of the entry's pieces
+            const char *blk = pool + (uint64_t)(uint32_t)(mapped ? raw : 0) * (uint64_t)blk_bytes +
+                              (int64_t)row0 * tok_bytes;
+            const int t_e = tok + 4 * PER_BLK * g;             // first row of the group's pieces
             if (mapped && t_e + 4 * PER_BLK <= ctx) {
 #pragma unroll
-                for (int jj = e * PER_BLK; jj < (e + 1) * PER_BLK; ++jj)
-                    load_lds_sbase<false>(blk + (int64_t)((4 * jj) % BS) * tok_bytes,
-                                          ld_row + (ld_unit ^ (16u * (jj & 3))), dst + 1024 * jj);
+                for (int i = 0; i < PER_BLK; ++i) {
+                    const int jj = g * PER_BLK + i;
+                    load_lds_sbase<false>(blk + (int64_t)(4 * i) * tok_bytes,
+                                          (ld_addr ^ (16u * (jj & 3))), dst + 1024 * jj);
+                }
             } else {
 #pragma unroll
-                for (int jj = e * PER_BLK; jj < (e + 1) * PER_BLK; ++jj) {
-                    const bool ok = mapped && tok + 4 * jj + (lane >> 4) < ctx;
-                    const char *src = blk + (int64_t)((4 * jj) % BS) * tok_bytes + ld_row + (ld_unit ^ (16u * (jj & 3)));
+                for (int i = 0; i < PER_BLK; ++i) {
+                    const int jj = g * PER_BLK + i;
+                    const bool ok = mapped && t_e + 4 * i + (lane >> 4) < ctx;
+                    const char *src = blk + (int64_t)(4 * i) * tok_bytes + (ld_addr ^ (16u * (jj & 3)));
                     load_lds_asm<false>(ok ? src : reinterpret_cast<const char *>(&wide_zero), dst + 1024 * jj);
                 }
             }
@@ -341,31 +362,31 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     // the products and the softmax of one step
     auto compute = [&](int t0, uint32_t okm, auto st_c) {
         constexpr int ST = decltype(st_c)::value;
-        const unsigned char PA_LDS *stg = lds + ST * WIDE_STAGE;
+        const unsigned char PA_LDS *stg = lds + ST * STAGE;
         // (a negative scale also takes the masked path: the other one takes the
         // max of the raw scores)
-        const bool masked = t0 + WIDE_STEP > t_full || t0 + WIDE_STEP > ctx || okm != (1u << NE) - 1u ||
+        const bool masked = t0 + SK > t_full || t0 + SK > ctx || okm != (1u << NE) - 1u ||
                             !(sl2 >= 0.f) || (MODE == WIDE_OWN && t0 < t_lo);
 
-        // all sixteen K fragments of the step are requested before the first
+        // all the K fragments of the step are requested before the first
         // product: the reads' latency is paid once per step, not per product
-        gqa_u32x4 kf[2][8];
+        gqa_u32x4 kf[KT][8];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int c = 0; c < 8; ++c)
-                kf[kt][c] = *reinterpret_cast<const gqa_u32x4 PA_LDS *>(stg + 8192 * kt + k_base + 16 * (k_x ^ (2 * c)));
+                kf[kt][c] = *reinterpret_cast<const gqa_u32x4 PA_LDS *>(stg + 8192 * kt + (k_addr ^ (32u * c)));
         __builtin_amdgcn_sched_barrier(0);
-        wide_f32x16 sc[2];
+        wide_f32x16 sc[KT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 sc[kt][v] = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
                 sc[kt] = WideOps<T>::mma(make_uint4(kf[kt][c].x, kf[kt][c].y, kf[kt][c].z, kf[kt][c].w), qb[c], sc[kt]);
 
         // the step's max of column j in log2 units, and the factor that takes
@@ -373,7 +394,7 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         float mx, f;
         if (masked) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int kr = 32 * kt + 8 * (v >> 2);             // first key of the 8-key group
@@ -383,7 +404,7 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
                 }
             mx = -INFINITY;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     mx = fmaxf(mx, sc[kt][v]);
@@ -391,7 +412,7 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         } else {
             float hi = sc[0][0];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     hi = fmaxf(hi, sc[kt][v]);
@@ -416,7 +437,7 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         }
 
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < NCH; ++c) {
             const int kt = c >> 1, v0 = 8 * (c & 1);
             float p[8];
 #pragma unroll
@@ -445,9 +466,9 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
             }
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const unsigned char PA_LDS *vs = stg + WIDE_TILE + 4096 * c;
-                const uint2 r0 = GqaOps<T>::read_tr(vs + (v_a + ((64u * dt) ^ v_b)));
-                const uint2 r1 = GqaOps<T>::read_tr(vs + 2048 + ((v_a ^ 32u) + ((64u * dt) ^ v_b)));
+                const unsigned char PA_LDS *vs = stg + TILE + 4096 * c;
+                const uint2 r0 = GqaOps<T>::read_tr(vs + (v_addr ^ (64u * dt)));
+                const uint2 r1 = GqaOps<T>::read_tr(vs + 2048 + (v_addr ^ (32u + 64u * dt)));
                 const uint4 va = make_uint4(r0.x, r0.y, r1.x, r1.y);
                 acc[dt] = WideOps<T>::mma(va, phi, acc[dt]);
                 if constexpr (HILO)
@@ -457,46 +478,91 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     };
 
     // one step out of stage ST (a constant, so that every LDS read takes its
-    // stage as an immediate offset: the loop below runs the steps in pairs)
-    // one step out of stage ST (a constant, so that every LDS read takes its
-    // stage as an immediate offset: the loop below runs the steps in pairs).
-    // ent_a holds the entries of this step, ent_b those of the next; the
-    // entries two steps ahead are fetched after the products, so that their
-    // scalar loads stay in flight across the barrier (which waits for vector
-    // loads only: every LDS read of the stage the next loads fill has been
-    // consumed by then)
-    int ent_a[NE], ent_b[NE];
+    // stage as an immediate offset: the loop below runs NST steps per turn).
+    // The loads run NST - 1 steps ahead: step t's tiles go to stage
+    // (t - s_first) % NST.  ent_n holds the table entries of the step the
+    // next issue loads; o0 .. o2 the in-pool blocks (bit e: keys e BS .. +BS)
+    // of this step and the next ones already issued.  The next entries are
+    // fetched after the products, so that their scalar loads stay in flight
+    // across the barrier (which waits for vector loads only: every LDS read
+    // of the stage the next loads fill has been consumed by then)
+    int ent_n[NE];
+    uint32_t o0 = 0u, o1 = 0u, o2 = 0u;
+    auto okm_of = [&](const int (&ent)[NE]) {
+        uint32_t o = 0u;
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            o |= ((unsigned)ent[e] < (unsigned)num_blocks ? 1u : 0u) << e;
+        return o;
+    };
     auto run_step = [&](int step, auto st_c) {
         constexpr int ST = decltype(st_c)::value;
-        // this wave's loads of the step have landed; at the barrier every
-        // wave's have, and every wave is done with the stage the next loads fill
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        if (step + 1 < n_steps)
-            issue(step + 1, ST ^ 1, ent_b);
-        // blocks of the step that lie in the pool (bit e: keys e BS .. +BS)
-        uint32_t okm = 0;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            okm |= ((unsigned)ent_a[e] < (unsigned)num_blocks ? 1u : 0u) << e;
-            ent_a[e] = ent_b[e];
+        // this wave's loads of the step have landed (those of the later steps
+        // already issued may still be in flight: loads complete in the order
+        // they were issued, PPW per step); at the barrier every wave's have,
+        // and every wave is done with the stage the next loads fill
+        const int later = min(NST - 2, n_steps - 1 - step);
+        if (later <= 0)
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        else if (later == 1)
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PPW) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * PPW) : "memory");
+        // one register per address family: the per-piece and per-fragment
+        // addresses are recomputed (one xor each) rather than kept live
+        asm volatile("" : "+v"(k_addr), "+v"(v_addr), "+v"(ld_addr));
+        if (step + NST - 1 < n_steps)
+            issue(step + NST - 1, (ST + NST - 1) % NST, ent_n);
+        const uint32_t okm = o0;
+        const uint32_t on = okm_of(ent_n);
+        if constexpr (NST == 2) {
+            o0 = on;
+        } else if constexpr (NST == 3) {
+            o0 = o1;
+            o1 = on;
+        } else {
+            o0 = o1;
+            o1 = o2;
+            o2 = on;
         }
-        const int t0 = step * WIDE_STEP;
+        const int t0 = step * SK;
         if (t0 < wave_end)
             compute(t0, okm, st_c);
-        if (step + 2 < n_steps)
-            fetch(step + 2, ent_b);
+        if (step + NST < n_steps)
+            fetch(step + NST, ent_n);
     };
 
     if (n_steps > s_first) {
-        fetch(s_first, ent_a);
-        if (n_steps > s_first + 1)
-            fetch(s_first + 1, ent_b);
-        issue(s_first, 0, ent_a);
+#pragma unroll
+        for (int i = 0; i < NST - 1; ++i) {
+            if (s_first + i < n_steps) {
+                int e0[NE];
+                fetch(s_first + i, e0);
+                issue(s_first + i, i, e0);
+                const uint32_t o = okm_of(e0);
+                if (i == 0)
+                    o0 = o;
+                else if (i == 1)
+                    o1 = o;
+                else
+                    o2 = o;
+            }
+        }
+        if (s_first + NST - 1 < n_steps)
+            fetch(s_first + NST - 1, ent_n);
     }
-    for (int step = s_first; step < n_steps; step += 2) {
+    for (int step = s_first; step < n_steps; step += NST) {
         run_step(step, std::integral_constant<int, 0>());
         if (step + 1 < n_steps)
             run_step(step + 1, std::integral_constant<int, 1>());
+        if constexpr (NST > 2) {
+            if (step + 2 < n_steps)
+                run_step(step + 2, std::integral_constant<int, 2 % NST>());
+        }
+        if constexpr (NST > 3) {
+            if (step + 3 < n_steps)
+                run_step(step + 3, std::integral_constant<int, 3 % NST>());
+        }
     }
 
     // every load into LDS has landed before the workgroup ends
