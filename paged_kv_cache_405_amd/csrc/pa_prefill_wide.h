@@ -486,7 +486,7 @@ __global__ __launch_bounds__(WIDE_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     // fetched after the products, so that their scalar loads stay in flight
     // across the barrier (which waits for vector loads only: every LDS read
     // of the stage the next loads fill has been consumed by then)
-    int ent_n[NE];
+    int ent_n[NE] = {};
     uint32_t o0 = 0u, o1 = 0u, o2 = 0u;
     auto okm_of = [&](const int (&ent)[NE]) {
         uint32_t o = 0u;
