@@ -61,6 +61,22 @@ def test_prefill_matches_the_oracle(dtype, D, bs, Hq, Hkv):
     assert_close(compare(out, ref, dtype), dtype, w.name)
 
 
+@pytest.mark.parametrize("dtype,bs", [("f16", 8), ("f16", 16), ("bf16", 16), ("bf16", 32)])
+def test_every_step_count_and_stage_phase(dtype, bs):
+    """head_dim 128: contexts from 1 to 257 tokens in steps of 8, so the workgroups run every number of 32-key
+    steps from 1 to 9 and end in every phase of the three-stage rotation, with chunks from one row to more rows
+    than one workgroup holds (each row's own causal limit)"""
+    ctxs = list(range(1, 258, 8))
+    counts = [min(c, 1 + (7 * i) % 150) for i, c in enumerate(ctxs)]
+    w = W.custom(f"prefill_steps_{dtype}_{bs}", dtype, ctxs, 8, 8, 128, bs, seed=300 + bs, append=False, table_pad=1)
+    rng = np.random.default_rng(301 + bs)
+    q_np = W.to_storage(rng.standard_normal((sum(counts), 8, 128), dtype=np.float32), dtype)
+    g = upload(w)
+    log(f"[gpu] prefill {w.name}")
+    out, ref = _run(w, g, q_np, counts)
+    assert_close(compare(out, ref, dtype), dtype, w.name)
+
+
 def test_rows_past_the_context_are_zero_and_bad_starts_touch_nothing():
     w = W.custom("prefill_edges", "bf16", [3, 0, 40], 16, 4, 128, 16, seed=77, append=False)
     rng = np.random.default_rng(78)
